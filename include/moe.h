@@ -1,0 +1,185 @@
+/*
+ * moe.h - C ABI of the routed Mixture-of-Experts feed-forward layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (pages: "MiMo V2.6 Pro and Flash architecture teardown",
+ * sections "What Did Xiaomi Release?", "How Big Is Each Expert?",
+ * "How Is the Backbone Built?", "Why Are the V2.6 Files Half the Size of
+ * V2.5?"; vLLM recipe "XiaomiMiMo/MiMo-V2.6-Pro-RL", section "Overview"):
+ *
+ *   L      = x . W_r^T                      bf16 router, fp32 logits
+ *   ids    = top-k of (L + b), k of E       ties -> lower expert id
+ *   w      = softmax of the k selected L    (b only steers selection)
+ *   for each routing slot (t, j), expert e = ids[t][j]:
+ *     a    = FP8(x[t])                      e4m3, one e8m0 scale per 128 ch.
+ *     g|u  = a . W13_e^T                    W13_e MXFP4 [2I, H]: gate rows, then up rows
+ *     h    = FP8(silu(g) * u)               e4m3, one e8m0 scale per 128 ch.
+ *     y_s  = h . W2_e^T                     W2_e MXFP4 [H, I]
+ *   y[t]   = sum_j w[t][j] * y_(t,j)        no shared expert
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *     caller; all layouts are row-major ("[A][B]": B contiguous).
+ *   - Work is enqueued on `stream` and runs asynchronously; no entry point
+ *     synchronises the host or allocates memory.  Entry points that need
+ *     scratch take a caller-provided workspace of at least
+ *     moe_workspace_size(problem) bytes (256-byte aligned).
+ *   - Outputs are fully overwritten (no pre-zeroing needed).  Inputs and
+ *     outputs must not alias.
+ *   - Argument errors are detected before anything is enqueued and returned
+ *     as a status; nothing is launched then.  A failed launch returns
+ *     MOE_ERR_HIP.  num_tokens == 0 returns MOE_OK and launches nothing.
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ *   - Pointers must be 16-byte aligned.
+ *   - Limits: hidden and intermediate multiples of 128, 1 <= num_experts
+ *     <= 512, 1 <= top_k <= min(num_experts, 8), num_tokens * top_k < 2^31.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same declaration as the HIP runtime's: a stream handle is an opaque pointer. */
+typedef struct ihipStream_t* hipStream_t;
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARGUMENT = 1,
+    MOE_ERR_UNSUPPORTED = 2,
+    MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOE_ERR_HIP = 4
+} moe_status;
+
+/* How combine weights are derived from the router logits.
+ * MOE_SCORE_SOFTMAX_TOPK: softmax over the k selected logits (the measured
+ * workloads).  Selection key = L + b (fp32 add), b optional. */
+typedef enum { MOE_SCORE_SOFTMAX_TOPK = 0 } moe_score_func;
+
+typedef enum { MOE_OUT_F32 = 0, MOE_OUT_BF16 = 1 } moe_out_dtype;
+
+typedef struct {
+    int64_t num_tokens;    /* T  */
+    int32_t hidden;        /* H  (multiple of 128) */
+    int32_t intermediate;  /* I  (multiple of 128), width of the expert middle layer */
+    int32_t num_experts;   /* E  */
+    int32_t top_k;         /* k  */
+    int32_t score_func;    /* moe_score_func */
+} moe_problem;
+
+/* MXFP4 expert weights ("two 4-bit values per byte (U8), one 8-bit scale per
+ * 32 values": teardown, "Why Are the V2.6 Files Half the Size of V2.5?").
+ * Element 2i of a row is in bits 3:0 of byte i, element 2i+1 in bits 7:4.
+ * Scales are e8m0 bytes (2^(b-127)), one per 32 consecutive elements of a row.
+ *   w13       [E][2I][H/2]   rows 0..I-1 gate, rows I..2I-1 up
+ *   w13_scale [E][2I][H/32]
+ *   w2        [E][H][I/2]
+ *   w2_scale  [E][H][I/32]                                                */
+typedef struct {
+    const uint8_t* w13;
+    const uint8_t* w13_scale;
+    const uint8_t* w2;
+    const uint8_t* w2_scale;
+} moe_expert_weights;
+
+/* ABI version (MOE_ABI_VERSION of the built library). */
+int moe_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char* moe_status_string(moe_status status);
+
+/* Workspace bytes every entry point of this header needs for `problem`
+ * (the maximum over entry points).  Returns 0 for an invalid problem. */
+size_t moe_workspace_size(const moe_problem* problem);
+
+/* Router and top-k selection (teardown, "How Big Is Each Expert?": a router
+ * picks 8 experts for each token; "Why Are the V2.6 Files Half the Size of
+ * V2.5?": BF16 router).
+ *   x_bf16        [T][H]  bf16 activations, or NULL
+ *   w_router_bf16 [E][H]  bf16 router weights, or NULL
+ *   sel_bias      [E]     fp32 selection bias, or NULL (= 0)
+ *   logits        [T][E]  fp32: OUTPUT (x . W_r^T, fp32 accumulation of the
+ *                         exact bf16 products) when x and w_router are given;
+ *                         INPUT when both are NULL (selection on given logits)
+ *   topk_ids      [T][k]  int32 out, descending key order, ties -> lower id
+ *   topk_w        [T][k]  fp32 out, softmax over the selected logits        */
+moe_status moe_route(const moe_problem* problem, const void* x_bf16, const void* w_router_bf16,
+                     const float* sel_bias, float* logits, int32_t* topk_ids, float* topk_w,
+                     hipStream_t stream);
+
+/* Permutation of the T*k routing slots by expert, and the FP8 activations in
+ * expert order.  Slots are s = t*k + j.  Rows of one expert keep ascending
+ * token order (a stable counting sort).
+ *   topk_ids       [T][k]       int32 in [0, E), distinct per token
+ *   x_bf16         [T][H]       bf16
+ *   expert_offsets [E+1]        int32 out: rows of expert e are [off[e], off[e+1])
+ *   sorted_token   [T*k]        int32 out: token of each expert-ordered row
+ *   row_of_slot    [T*k]        int32 out: expert-ordered row of each slot
+ *   xq_perm        [T*k][H]     e4m3 out: FP8 codes of x[sorted_token[r]]
+ *   xs_perm        [T*k][H/128] e8m0 out: per-128-channel power-of-two scale
+ * The FP8 rule: amax of each 128-channel run, scale 2^e with e the smallest
+ * integer such that amax / 2^e <= 448, codes = round-to-nearest-even e4m3 of
+ * x / 2^e (an all-zero run gets scale byte 0).                            */
+moe_status moe_permute(const moe_problem* problem, const int32_t* topk_ids, const void* x_bf16,
+                       int32_t* expert_offsets, int32_t* sorted_token, int32_t* row_of_slot,
+                       uint8_t* xq_perm, uint8_t* xs_perm, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* The experts on their rows: gate/up projection, SwiGLU, FP8 requantisation
+ * of h, down projection (teardown, "How Big Is Each Expert?": gate, up and
+ * down projections around a 2,048-wide middle; vLLM recipe "Overview": FP8
+ * compute of MXFP4-stored weights).
+ *   xq_perm, xs_perm, expert_offsets  as produced by moe_permute
+ *   y_perm [T*k][H] fp32 out: expert output of each row (unweighted)       */
+moe_status moe_grouped_gemm_swiglu(const moe_problem* problem, const uint8_t* xq_perm,
+                                   const uint8_t* xs_perm, const int32_t* expert_offsets,
+                                   const moe_expert_weights* weights, float* y_perm,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* First half of moe_grouped_gemm_swiglu: gate/up projection, SwiGLU
+ * h = silu(g) * u with silu(z) = z / (1 + e^-z), and FP8 quantisation of h
+ * with the rule of moe_permute.
+ *   hq_perm [T*k][I] e4m3 out, hs_perm [T*k][I/128] e8m0 out              */
+moe_status moe_grouped_gemm1_swiglu(const moe_problem* problem, const uint8_t* xq_perm,
+                                    const uint8_t* xs_perm, const int32_t* expert_offsets,
+                                    const moe_expert_weights* weights, uint8_t* hq_perm,
+                                    uint8_t* hs_perm, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Gate/up pre-activations only (for exactness checks of the block-scaled
+ * product): gu_perm [T*k][2I] fp32 out, columns 0..I-1 gate, I..2I-1 up.  */
+moe_status moe_grouped_gemm1_preact(const moe_problem* problem, const uint8_t* xq_perm,
+                                    const uint8_t* xs_perm, const int32_t* expert_offsets,
+                                    const moe_expert_weights* weights, float* gu_perm,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Second half of moe_grouped_gemm_swiglu: y_perm = h . W2_e^T per row.     */
+moe_status moe_grouped_gemm2(const moe_problem* problem, const uint8_t* hq_perm,
+                             const uint8_t* hs_perm, const int32_t* expert_offsets,
+                             const moe_expert_weights* weights, float* y_perm,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Weighted combine: y[t] = sum_{j=0..k-1} topk_w[t][j] * y_perm[row_of_slot[t*k+j]],
+ * accumulated in fp32 in slot order; out_dtype MOE_OUT_BF16 stores the
+ * round-to-nearest-even bf16 of that fp32 sum.
+ *   y [T][H] fp32 or bf16 out                                             */
+moe_status moe_combine(const moe_problem* problem, const float* y_perm, const int32_t* row_of_slot,
+                       const float* topk_w, void* y, int32_t out_dtype, hipStream_t stream);
+
+/* The whole layer: moe_route, moe_permute, moe_grouped_gemm_swiglu and
+ * moe_combine in one stream, all intermediates in the workspace.          */
+moe_status moe_forward(const moe_problem* problem, const void* x_bf16, const void* w_router_bf16,
+                       const float* sel_bias, const moe_expert_weights* weights, void* y,
+                       int32_t out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -83,6 +83,9 @@ def decode_e4m3(byte):
     return np.where(s == 1, -mag, mag)
 
 
+_E2M1_VALUES = decode_e2m1(np.arange(16))   # the 16 values, indexed by code
+
+
 def unpack_fp4(packed):
     """[..., K/2] uint8 -> [..., K] nibbles; element 2i is the low nibble, 2i+1 the high one."""
     p = np.asarray(packed, dtype=np.uint8)
@@ -99,7 +102,7 @@ def decode_mxfp4(codes, scales):
     scales [R, K/32] uint8 (e8m0, one per 32 consecutive K elements of a row)
     returns [R, K] float64, each element = e2m1 value * its group's scale.
     """
-    vals = decode_e2m1(unpack_fp4(codes))
+    vals = _E2M1_VALUES[unpack_fp4(codes)]
     sc = decode_e8m0(scales)
     return vals * np.repeat(sc, MX_BLOCK, axis=-1)
 

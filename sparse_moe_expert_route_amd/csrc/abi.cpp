@@ -1,0 +1,287 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace carving and the launch sequence of each entry point.
+//
+// Nothing here allocates, synchronises or throws; every check happens before
+// the first launch, so a rejected call enqueues nothing.
+#include <hip/hip_runtime_api.h>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+    size_t logits, ids, w, offsets, sorted_token, row_of_slot, block_counts, block_base, tile_start;
+    size_t xq, xs, hq, hs, y_perm, total;
+};
+
+moe_status check_problem(const moe_problem* p) {
+    if (!p) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_tokens < 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->hidden <= 0 || p->hidden % kFp8Block) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->intermediate <= 0 || p->intermediate % kFp8Block) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_experts < 1 || p->num_experts > 512) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->top_k < 1 || p->top_k > 8 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->score_func != MOE_SCORE_SOFTMAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (p->num_tokens * (int64_t)p->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+Layout layout_of(const moe_problem& p) {
+    const size_t T = (size_t)p.num_tokens, k = (size_t)p.top_k, N = T * k;
+    const size_t E = (size_t)p.num_experts, H = (size_t)p.hidden, I = (size_t)p.intermediate;
+    const size_t nblk = N ? (N + kPermBlock - 1) / kPermBlock : 1;
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes ? bytes : 1); return o; };
+    L.logits = take(T * E * 4);
+    L.ids = take(N * 4);
+    L.w = take(N * 4);
+    L.offsets = take((E + 1) * 4);
+    L.sorted_token = take(N * 4);
+    L.row_of_slot = take(N * 4);
+    L.block_counts = take(nblk * E * 4);
+    L.block_base = take(nblk * E * 4);
+    L.tile_start = take((E + 1) * 4);
+    L.xq = take(N * H);
+    L.xs = take(N * (H / kFp8Block));
+    L.hq = take(N * I);
+    L.hs = take(N * (I / kFp8Block));
+    L.y_perm = take(N * H * 4);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+moe_status check_ws(const moe_problem& p, const void* ws, size_t ws_bytes) {
+    if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)ws % kAlign) != 0) return MOE_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < layout_of(p).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_expert_weights* w) {
+    if (!w || !w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w->w13) || !aligned16(w->w13_scale) || !aligned16(w->w2) || !aligned16(w->w2_scale))
+        return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
+#define MOE_CHECK(expr)                          \
+    do {                                         \
+        const moe_status st_ = (expr);           \
+        if (st_ != MOE_OK) return st_;           \
+    } while (0)
+#define MOE_LAUNCH(expr)                         \
+    do {                                         \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+bool all_aligned() { return true; }
+template <typename P, typename... R>
+bool all_aligned(P p, R... rest) { return p && aligned16(p) && all_aligned(rest...); }
+
+// ---- launch sequences (arguments already validated) ----------------------
+
+moe_status run_route(const moe_problem& p, const void* x, const void* wr, const float* bias, float* logits,
+                     int32_t* ids, float* w, hipStream_t stream) {
+    if (x) MOE_LAUNCH(launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, logits, p.num_tokens, p.hidden,
+                                           p.num_experts, stream));
+    MOE_LAUNCH(launch_topk(logits, bias, ids, w, p.num_tokens, p.num_experts, p.top_k, stream));
+    return MOE_OK;
+}
+
+moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, int32_t* offsets,
+                       int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, uint8_t* xs, void* ws,
+                       hipStream_t stream) {
+    const Layout L = layout_of(p);
+    const int64_t N = p.num_tokens * p.top_k;
+    int32_t* bc = at<int32_t>(ws, L.block_counts);
+    int32_t* bb = at<int32_t>(ws, L.block_base);
+    MOE_LAUNCH(launch_perm_count(ids, bc, N, p.num_experts, stream));
+    MOE_LAUNCH(launch_perm_scan(bc, bb, offsets, N, p.num_experts, stream));
+    MOE_LAUNCH(launch_perm_scatter(ids, bb, offsets, sorted_token, row_of_slot, N, p.num_experts, p.top_k, stream));
+    MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens, stream));
+    return MOE_OK;
+}
+
+GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_scale, const int32_t* offsets,
+                   const int32_t* tile_start, const uint8_t* w, const uint8_t* w_scale, void* out,
+                   uint8_t* out_scale) {
+    GemmArgs a;
+    a.act = act; a.act_scale = act_scale; a.offsets = offsets; a.tile_start = tile_start;
+    a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = out_scale;
+    a.N = p.num_tokens * p.top_k;
+    a.H = p.hidden; a.I = p.intermediate; a.E = p.num_experts;
+    return a;
+}
+
+moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, const uint8_t* xs,
+                     const int32_t* offsets, const moe_expert_weights& wt, void* out, uint8_t* out_scale,
+                     void* ws, bool plan, hipStream_t stream) {
+    const Layout L = layout_of(p);
+    int32_t* ts = at<int32_t>(ws, L.tile_start);
+    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, kRowsPerTile, stream));
+    MOE_LAUNCH(launch_expert_gemm(mode, gemm_args(p, xq, xs, offsets, ts, wt.w13, wt.w13_scale, out, out_scale),
+                                  stream));
+    return MOE_OK;
+}
+
+moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const uint8_t* hs, const int32_t* offsets,
+                     const moe_expert_weights& wt, float* y_perm, void* ws, bool plan, hipStream_t stream) {
+    const Layout L = layout_of(p);
+    int32_t* ts = at<int32_t>(ws, L.tile_start);
+    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, kRowsPerTile, stream));
+    MOE_LAUNCH(launch_expert_gemm(kGemm2, gemm_args(p, hq, hs, offsets, ts, wt.w2, wt.w2_scale, y_perm, nullptr),
+                                  stream));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported problem";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP launch failure";
+    }
+    return "unknown status";
+}
+
+size_t moe_workspace_size(const moe_problem* p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return layout_of(*p).total;
+}
+
+moe_status moe_route(const moe_problem* p, const void* x_bf16, const void* w_router_bf16, const float* sel_bias,
+                     float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    if ((x_bf16 == nullptr) != (w_router_bf16 == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+    if (x_bf16 && !all_aligned(x_bf16, w_router_bf16)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!all_aligned(logits, topk_ids, topk_w)) return MOE_ERR_INVALID_ARGUMENT;
+    if (sel_bias && !aligned16(sel_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_tokens == 0) return MOE_OK;
+    return run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, topk_ids, topk_w, stream);
+}
+
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, const void* x_bf16, int32_t* expert_offsets,
+                       int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq_perm, uint8_t* xs_perm,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    if (!all_aligned(topk_ids, x_bf16, expert_offsets, sorted_token, row_of_slot, xq_perm, xs_perm))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_ws(*p, ws, ws_bytes));
+    if (p->num_tokens == 0) return MOE_OK;
+    return run_permute(*p, topk_ids, x_bf16, expert_offsets, sorted_token, row_of_slot, xq_perm, xs_perm, ws, stream);
+}
+
+moe_status moe_grouped_gemm1_swiglu(const moe_problem* p, const uint8_t* xq_perm, const uint8_t* xs_perm,
+                                    const int32_t* expert_offsets, const moe_expert_weights* weights,
+                                    uint8_t* hq_perm, uint8_t* hs_perm, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (!all_aligned(xq_perm, xs_perm, expert_offsets, hq_perm, hs_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_ws(*p, ws, ws_bytes));
+    if (p->num_tokens == 0) return MOE_OK;
+    return run_gemm1(*p, kGemm1Swiglu, xq_perm, xs_perm, expert_offsets, *weights, hq_perm, hs_perm, ws, true,
+                     stream);
+}
+
+moe_status moe_grouped_gemm1_preact(const moe_problem* p, const uint8_t* xq_perm, const uint8_t* xs_perm,
+                                    const int32_t* expert_offsets, const moe_expert_weights* weights,
+                                    float* gu_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (!all_aligned(xq_perm, xs_perm, expert_offsets, gu_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_ws(*p, ws, ws_bytes));
+    if (p->num_tokens == 0) return MOE_OK;
+    return run_gemm1(*p, kGemm1Preact, xq_perm, xs_perm, expert_offsets, *weights, gu_perm, nullptr, ws, true,
+                     stream);
+}
+
+moe_status moe_grouped_gemm2(const moe_problem* p, const uint8_t* hq_perm, const uint8_t* hs_perm,
+                             const int32_t* expert_offsets, const moe_expert_weights* weights, float* y_perm,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (!all_aligned(hq_perm, hs_perm, expert_offsets, y_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_ws(*p, ws, ws_bytes));
+    if (p->num_tokens == 0) return MOE_OK;
+    return run_gemm2(*p, hq_perm, hs_perm, expert_offsets, *weights, y_perm, ws, true, stream);
+}
+
+moe_status moe_grouped_gemm_swiglu(const moe_problem* p, const uint8_t* xq_perm, const uint8_t* xs_perm,
+                                   const int32_t* expert_offsets, const moe_expert_weights* weights, float* y_perm,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (!all_aligned(xq_perm, xs_perm, expert_offsets, y_perm)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_ws(*p, ws, ws_bytes));
+    if (p->num_tokens == 0) return MOE_OK;
+    const Layout L = layout_of(*p);
+    uint8_t* hq = at<uint8_t>(ws, L.hq);
+    uint8_t* hs = at<uint8_t>(ws, L.hs);
+    MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq_perm, xs_perm, expert_offsets, *weights, hq, hs, ws, true, stream));
+    return run_gemm2(*p, hq, hs, expert_offsets, *weights, y_perm, ws, false, stream);
+}
+
+moe_status moe_combine(const moe_problem* p, const float* y_perm, const int32_t* row_of_slot, const float* topk_w,
+                       void* y, int32_t out_dtype, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (!all_aligned(y_perm, row_of_slot, topk_w, y)) return MOE_ERR_INVALID_ARGUMENT;
+    if (p->num_tokens == 0) return MOE_OK;
+    MOE_LAUNCH(launch_combine(y_perm, row_of_slot, topk_w, y, out_dtype == MOE_OUT_BF16, p->num_tokens, p->hidden,
+                              p->top_k, stream));
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_router_bf16, const float* sel_bias,
+                       const moe_expert_weights* weights, void* y, int32_t out_dtype, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (!all_aligned(x_bf16, w_router_bf16, y)) return MOE_ERR_INVALID_ARGUMENT;
+    if (sel_bias && !aligned16(sel_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_ws(*p, ws, ws_bytes));
+    if (p->num_tokens == 0) return MOE_OK;
+    const Layout L = layout_of(*p);
+    float* logits = at<float>(ws, L.logits);
+    int32_t* ids = at<int32_t>(ws, L.ids);
+    float* w = at<float>(ws, L.w);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* st = at<int32_t>(ws, L.sorted_token);
+    int32_t* ros = at<int32_t>(ws, L.row_of_slot);
+    uint8_t* xq = at<uint8_t>(ws, L.xq);
+    uint8_t* xs = at<uint8_t>(ws, L.xs);
+    uint8_t* hq = at<uint8_t>(ws, L.hq);
+    uint8_t* hs = at<uint8_t>(ws, L.hs);
+    float* y_perm = at<float>(ws, L.y_perm);
+    MOE_CHECK(run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, ids, w, stream));
+    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream));
+    MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq, xs, offsets, *weights, hq, hs, ws, true, stream));
+    MOE_CHECK(run_gemm2(*p, hq, hs, offsets, *weights, y_perm, ws, false, stream));
+    MOE_LAUNCH(launch_combine(y_perm, ros, w, y, out_dtype == MOE_OUT_BF16, p->num_tokens, p->hidden, p->top_k,
+                              stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Internal declarations shared by the HIP translation units of the MoE library.
+// Not part of the public ABI (include/moe.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kFp8Block = 128;   // channels per activation scale
+constexpr int kMxBlock = 32;     // weight elements per e8m0 scale
+constexpr int kPermBlock = 1024; // routing slots per block of the permutation kernels
+
+// ---------------------------------------------------------------------------
+// FP8 block quantisation rule (shared by the activation quantiser and the
+// SwiGLU epilogue): scale 2^e with e the smallest integer such that
+// amax / 2^e <= 448 = 1.75 * 2^8; written as e8m0 byte e + 127.  With
+// amax = m * 2^x, m in [0.5, 1): e = x - 9 if m <= 0.875, else x - 8.
+// An all-zero block gets e = -127 (byte 0).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int fp8_block_exponent(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    int x = __builtin_amdgcn_frexp_expf(amax);
+    float m = __builtin_amdgcn_frexp_mantf(amax);
+    int e = (m <= 0.875f) ? x - 9 : x - 8;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Four floats (already divided by their block scale, |v| <= 448) -> four
+// e4m3 bytes, round to nearest even (v_cvt_pk_fp8_f32), byte i = v[i].
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
+    return __uint_as_float(b16 << 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Block-scaled MFMA, A = FP4 (e2m1) weights, B = FP8 (e4m3) activations:
+// D[16 weight rows][16 tokens] += sum_k A[row][k] * B[token][k] over 128 k.
+template <int OPSEL_A>
+__device__ __forceinline__ v4f mfma_w4a8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, OPSEL_A, scale_a, 0, scale_b);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (host side).  Every launcher enqueues on `stream` and returns the
+// launch status; shapes are validated by the caller.
+// ---------------------------------------------------------------------------
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, float* logits,
+                                int64_t T, int H, int E, hipStream_t stream);
+hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w,
+                       int64_t T, int E, int k, hipStream_t stream);
+
+hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
+                             hipStream_t stream);
+hipError_t launch_perm_scan(const int32_t* block_counts, int32_t* block_base, int32_t* offsets,
+                            int64_t N, int E, hipStream_t stream);
+hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, const int32_t* offsets,
+                               int32_t* sorted_token, int32_t* row_of_slot, int64_t N, int E, int k,
+                               hipStream_t stream);
+hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq,
+                               uint8_t* xs, int64_t N, int H, int64_t T, hipStream_t stream);
+
+hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int E, int rows_per_tile,
+                            hipStream_t stream);
+
+enum GemmMode { kGemm1Swiglu = 0, kGemm1Preact = 1, kGemm2 = 2 };
+
+// Grouped expert GEMM over the expert-ordered rows.  For gemm1 modes the
+// weights are W13 [E][2I][H/2] and K = H; for gemm2 they are W2 [E][H][I/2]
+// and K = I.
+struct GemmArgs {
+    const uint8_t* act;        // [N][K] e4m3
+    const uint8_t* act_scale;  // [N][K/128] e8m0
+    const int32_t* offsets;    // [E+1]
+    const int32_t* tile_start; // [E+1], tiles of kRowsPerTile rows
+    const uint8_t* w;          // codes
+    const uint8_t* w_scale;    // e8m0 per 32
+    void* out;                 // swiglu: hq [N][I] + hs; preact: float [N][2I]; gemm2: float [N][H]
+    uint8_t* out_scale;        // swiglu: hs [N][I/128]
+    int64_t N;
+    int H, I, E;
+};
+constexpr int kRowsPerTile = 16;   // rows per m-tile of the streaming expert GEMM
+hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y,
+                          int out_bf16, int64_t T, int H, int k, hipStream_t stream);
+
+}  // namespace moe

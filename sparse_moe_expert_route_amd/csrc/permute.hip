@@ -1,0 +1,200 @@
+// Expert permutation of the routing slots (histogram, prefix scan, stable
+// rank) and the dynamic FP8 quantisation of activations gathered into expert
+// order.
+//
+// Slots are s = t*k + j.  Rows of one expert keep ascending slot (hence
+// token) order, so the result is deterministic: no atomic decides a row.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Pass 1: per-block expert histogram of kPermBlock slots (LDS atomics only
+// count; they decide no position).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) perm_count_kernel(const int32_t* __restrict__ ids,
+                                                          int32_t* __restrict__ block_counts,
+                                                          int N, int E) {
+    __shared__ int cnt[512];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    __syncthreads();
+    const int s = blockIdx.x * kPermBlock + threadIdx.x;
+    if (s < N) {
+        const int e = ids[s];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // out-of-range ids are dropped
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2 (one workgroup): for each expert, the exclusive prefix over blocks
+// (block_base), then the exclusive prefix over experts of the totals
+// (offsets[0..E], offsets[E] = N).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(512) perm_scan_kernel(const int32_t* __restrict__ block_counts,
+                                                        int32_t* __restrict__ block_base,
+                                                        int32_t* __restrict__ offsets, int nblk, int E) {
+    __shared__ int tot[512];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int b = 0; b < nblk; ++b) {
+            const int c = block_counts[(size_t)b * E + e];
+            block_base[(size_t)b * E + e] = run;
+            run += c;
+        }
+    }
+    tot[e] = (e < E) ? run : 0;
+    __syncthreads();
+    // Hillis-Steele inclusive scan over 512 entries
+    for (int d = 1; d < 512; d <<= 1) {
+        const int v = (e >= d) ? tot[e - d] : 0;
+        __syncthreads();
+        tot[e] += v;
+        __syncthreads();
+    }
+    if (e < E) offsets[e] = tot[e] - run;
+    if (e == E - 1) offsets[E] = tot[e];
+}
+
+// ---------------------------------------------------------------------------
+// Pass 3: row of every slot = offsets[e] + block_base[b][e] + (slots of e in
+// earlier waves of this block) + (slots of e in earlier lanes of this wave).
+// The in-wave match mask is built from one ballot per bit of the expert id.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __restrict__ ids,
+                                                            const int32_t* __restrict__ block_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_token,
+                                                            int32_t* __restrict__ row_of_slot,
+                                                            int N, int E, int k) {
+    __shared__ int wcnt[16][512];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 16 * 512; i += blockDim.x) (&wcnt[0][0])[i] = 0;
+    const int s = blockIdx.x * kPermBlock + threadIdx.x;
+    const int id = s < N ? ids[s] : -1;
+    const bool valid = (unsigned)id < (unsigned)E;
+    const int e = valid ? id : 1023;   // 1023 never equals a real id (E <= 512)
+
+    unsigned long long m = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+        const unsigned long long b = __ballot((e >> bit) & 1);
+        m &= ((e >> bit) & 1) ? b : ~b;
+    }
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(m & lt);
+    __syncthreads();   // wcnt cleared
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (!valid) {
+        if (s < N) row_of_slot[s] = -1;   // an out-of-range id gets no row
+        return;
+    }
+    int pre = 0;
+    for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+    const int row = offsets[e] + block_base[(size_t)blockIdx.x * E + e] + pre + rank;
+    row_of_slot[s] = row;
+    sorted_token[row] = s / k;
+}
+
+hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
+                             hipStream_t stream) {
+    const int nblk = (int)((N + kPermBlock - 1) / kPermBlock);
+    hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(kPermBlock), 0, stream, ids, block_counts, (int)N, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_scan(const int32_t* block_counts, int32_t* block_base, int32_t* offsets, int64_t N,
+                            int E, hipStream_t stream) {
+    const int nblk = (int)((N + kPermBlock - 1) / kPermBlock);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(512), 0, stream, block_counts, block_base, offsets, nblk, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, const int32_t* offsets,
+                               int32_t* sorted_token, int32_t* row_of_slot, int64_t N, int E, int k,
+                               hipStream_t stream) {
+    const int nblk = (int)((N + kPermBlock - 1) / kPermBlock);
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(kPermBlock), 0, stream, ids, block_base, offsets,
+                       sorted_token, row_of_slot, (int)N, E, k);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Quantise + gather: row r of the output is FP8(x[sorted_token[r]]).
+// 256 threads per row, 8 channels (one 16-byte bf16 load) per thread, so a
+// 128-channel block is 16 consecutive lanes: amax by xor-shuffles within the
+// 16, then the shared block exponent, then RNE e4m3 codes of x * 2^-e
+// (an exact power-of-two scaling).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) quant_gather_kernel(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ sorted_token,
+                                                           uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                           int N, int H, int T) {
+    for (int r = blockIdx.x; r < N; r += gridDim.x) {
+        const int t = min(max(sorted_token[r], 0), T - 1);   // rows left unfilled by invalid ids stay in bounds
+        const uint16_t* xr = x + (size_t)t * H;
+        uint8_t* qr = xq + (size_t)r * H;
+        for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
+            const uint4 raw = *(const uint4*)(xr + c);
+            float v[8];
+            v[0] = bf16_bits_to_float(raw.x & 0xFFFFu); v[1] = bf16_bits_to_float(raw.x >> 16);
+            v[2] = bf16_bits_to_float(raw.y & 0xFFFFu); v[3] = bf16_bits_to_float(raw.y >> 16);
+            v[4] = bf16_bits_to_float(raw.z & 0xFFFFu); v[5] = bf16_bits_to_float(raw.z >> 16);
+            v[6] = bf16_bits_to_float(raw.w & 0xFFFFu); v[7] = bf16_bits_to_float(raw.w >> 16);
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+            const int e = fp8_block_exponent(amax);
+            float q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_ldexpf(v[i], -e);
+            uint2 codes;
+            codes.x = pack_fp8x4(q[0], q[1], q[2], q[3]);
+            codes.y = pack_fp8x4(q[4], q[5], q[6], q[7]);
+            *(uint2*)(qr + c) = codes;
+            if ((threadIdx.x & 15) == 0) xs[(size_t)r * (H / kFp8Block) + c / kFp8Block] = (uint8_t)(e + 127);
+        }
+    }
+}
+
+hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq, uint8_t* xs,
+                               int64_t N, int H, int64_t T, hipStream_t stream) {
+    const int grid = (int)(N < 65536 ? N : 65536);
+    hipLaunchKernelGGL(quant_gather_kernel, dim3(grid), dim3(256), 0, stream, x, sorted_token, xq, xs, (int)N, H,
+                       (int)T);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Tile plan of the grouped GEMMs: expert e owns m-tiles
+// [tile_start[e], tile_start[e+1]) of rows_per_tile rows each.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ tile_start, int E, int rpt) {
+    __shared__ int tot[512];
+    const int e = threadIdx.x;
+    const int n = (e < E) ? (offsets[e + 1] - offsets[e] + rpt - 1) / rpt : 0;
+    tot[e] = n;
+    __syncthreads();
+    for (int d = 1; d < 512; d <<= 1) {
+        const int v = (e >= d) ? tot[e - d] : 0;
+        __syncthreads();
+        tot[e] += v;
+        __syncthreads();
+    }
+    if (e < E) tile_start[e] = tot[e] - n;
+    if (e == E - 1) tile_start[E] = tot[e];
+}
+
+hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int E, int rows_per_tile,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(512), 0, stream, offsets, tile_start, E, rows_per_tile);
+    return hipGetLastError();
+}
+
+}  // namespace moe

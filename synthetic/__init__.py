@@ -144,15 +144,18 @@ def zipf_bias(E, H, seed=0):
     return (-0.55 * sigma * np.log(r)).astype(np.float32)
 
 
-def make_layer(name_or_cfg, seed=0, **over):
-    """All inputs of one layer as numpy arrays (see the module docstring for distributions)."""
+def make_layer(name_or_cfg, seed=0, experts=True, **over):
+    """All inputs of one layer as numpy arrays (see the module docstring for distributions).
+
+    experts=False skips the expert weights (for router-only uses)."""
     cfg = config(name_or_cfg, **over)
     T, H, E, k, inter = cfg["T"], cfg["H"], cfg["E"], cfg["k"], cfg["I"]
     layer = dict(cfg=cfg, top_k=k)
     layer["x"] = bf16_normal(seed, STREAM_X, (T, H), 1.0)
     layer["w_router"] = bf16_normal(seed, STREAM_WR, (E, H), 0.02)
-    layer["w13"], layer["w13_s"] = mxfp4_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
-    layer["w2"], layer["w2_s"] = mxfp4_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
+    if experts:
+        layer["w13"], layer["w13_s"] = mxfp4_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
+        layer["w2"], layer["w2_s"] = mxfp4_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
     if cfg["bias"] == "zipf":
         layer["bias"] = zipf_bias(E, H, seed)
     elif cfg["bias"] == "zero":
