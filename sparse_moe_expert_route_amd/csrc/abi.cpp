@@ -126,25 +126,36 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_
     return a;
 }
 
+// Weight-streaming kernel when experts get few rows (decode); LDS-tiled
+// kernel when the average expert has at least 32 rows (prefill).  The choice
+// depends on host-known sizes only, so both GEMMs of one call agree on it.
+bool use_tiled(const moe_problem& p) {
+    return tiled_gemm_supported(p.hidden, p.intermediate) &&
+           p.num_tokens * p.top_k >= 32 * (int64_t)p.num_experts;
+}
+
+moe_status launch_gemm(const moe_problem& p, GemmMode mode, const GemmArgs& a, hipStream_t stream) {
+    MOE_LAUNCH(use_tiled(p) ? launch_expert_gemm_tiled(mode, a, stream) : launch_expert_gemm(mode, a, stream));
+    return MOE_OK;
+}
+
 moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, const uint8_t* xs,
                      const int32_t* offsets, const moe_expert_weights& wt, void* out, uint8_t* out_scale,
                      void* ws, bool plan, hipStream_t stream) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
-    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, kRowsPerTile, stream));
-    MOE_LAUNCH(launch_expert_gemm(mode, gemm_args(p, xq, xs, offsets, ts, wt.w13, wt.w13_scale, out, out_scale),
-                                  stream));
-    return MOE_OK;
+    const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
+    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, rpt, stream));
+    return launch_gemm(p, mode, gemm_args(p, xq, xs, offsets, ts, wt.w13, wt.w13_scale, out, out_scale), stream);
 }
 
 moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const uint8_t* hs, const int32_t* offsets,
                      const moe_expert_weights& wt, float* y_perm, void* ws, bool plan, hipStream_t stream) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
-    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, kRowsPerTile, stream));
-    MOE_LAUNCH(launch_expert_gemm(kGemm2, gemm_args(p, hq, hs, offsets, ts, wt.w2, wt.w2_scale, y_perm, nullptr),
-                                  stream));
-    return MOE_OK;
+    const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
+    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, rpt, stream));
+    return launch_gemm(p, kGemm2, gemm_args(p, hq, hs, offsets, ts, wt.w2, wt.w2_scale, y_perm, nullptr), stream);
 }
 
 }  // namespace

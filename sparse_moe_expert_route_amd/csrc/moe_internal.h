@@ -98,6 +98,12 @@ struct GemmArgs {
 constexpr int kRowsPerTile = 16;   // rows per m-tile of the streaming expert GEMM
 hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream);
 
+// LDS-tiled variant for many rows per expert: m-tiles of 128 rows, needs
+// H and I multiples of 256.
+constexpr int kRowsPerTileTiled = 128;
+bool tiled_gemm_supported(int H, int I);
+hipError_t launch_expert_gemm_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream);
+
 hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y,
                           int out_bf16, int64_t T, int H, int k, hipStream_t stream);
 

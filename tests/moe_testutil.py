@@ -150,6 +150,8 @@ def h_rounding_allowance(a, w13_e, w13_s_e, w2_e, w2_s_e, acc_rel=ACC_REL):
     cross_up = v + dv >= q + up / 2
     cross_dn = (v - dv <= q - dn / 2) & (q > 0)
     allow_el = np.where(cross_up, up, 0.0) + np.where(cross_dn, dn, 0.0)
+    # an interval around 0 can round to either sign: the code may be any of the smallest codes of either sign
+    allow_el = np.where(v <= dv, np.maximum(allow_el, q + up), allow_el)
     # block scale: the exponent changes if the amax interval reaches the 1.75 * 2^q threshold
     blk = lambda z: z.reshape(R, C // 128, 128)
     amax = blk(np.abs(h)).max(-1)

@@ -57,7 +57,8 @@ def _forward(moe, lay, p, W, out_dtype=0, ws=None):
 
 SMALL = [("tiny", {}), ("tiny", dict(bias="zipf", E=32, k=4, T=100)), ("tiny", dict(T=1)),
          ("tiny", dict(E=4, k=4, T=33)), ("tiny", dict(k=1, T=70)), ("tiny", dict(T=129, H=512, I=256, E=24, k=8)),
-         ("tiny", dict(T=40, H=1024, I=640, E=12, k=3))]
+         ("tiny", dict(T=40, H=1024, I=640, E=12, k=3)),
+         ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf")), ("tiny", dict(T=300, H=256, I=256, E=8, k=8))]
 
 
 @pytest.mark.parametrize("cfg,over", SMALL)

@@ -151,9 +151,12 @@ def _offsets_for(T, E, k, seed, skew=None):
     return OL.permutation(ids, E)["offsets"]
 
 
+# the first five shapes run the weight-streaming kernel (few rows per expert),
+# the last three the LDS-tiled kernel (>= 32 rows per expert on average)
 @pytest.mark.parametrize("T,H,I,E,k,skew", [(64, 256, 128, 8, 2, None), (40, 512, 256, 16, 4, 3.0),
                                             (9, 4096, 2048, 8, 8, None), (150, 1024, 384, 12, 3, 2.0),
-                                            (3, 6144, 256, 4, 2, None)])
+                                            (3, 6144, 256, 4, 2, None), (300, 512, 512, 8, 4, 2.0),
+                                            (200, 1024, 256, 16, 8, None), (700, 256, 768, 8, 2, 6.0)])
 def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
     log("gemm1 lossless T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
     N = T * k
@@ -176,7 +179,7 @@ def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 8, 2), (40, 512, 256, 16, 4), (9, 4096, 2048, 8, 8),
-                                       (33, 384, 640, 5, 2)])
+                                       (33, 384, 640, 5, 2), (300, 512, 512, 8, 4), (200, 1280, 256, 16, 8)])
 def test_gemm2_lossless_bitexact(moe, T, H, I, E, k):
     log("gemm2 lossless T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
     N = T * k
@@ -202,7 +205,8 @@ def test_gemm2_lossless_bitexact(moe, T, H, I, E, k):
 # SwiGLU + FP8 requantisation epilogue on random operands
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,over", [("tiny", {}), ("tiny", dict(T=90, H=512, I=384, E=16, k=4)),
-                                      ("flash_decode", dict(E=16, T=24))])
+                                      ("flash_decode", dict(E=16, T=24)), ("tiny", dict(T=400, H=512, I=512, E=8, k=4)),
+                                      ("flash_decode", dict(E=8, T=160))])
 def test_gemm1_swiglu_parity(moe, cfg, over):
     lay = S.make_layer(cfg, seed=5, **over)
     T, H = lay["x"].shape
@@ -235,7 +239,9 @@ def test_gemm1_swiglu_parity(moe, cfg, over):
     # the scale decision agrees except where the float64 block maximum sits on a power-of-two boundary
     assert np.mean(gs == ref_s) > 0.999
     same = np.repeat(gs == ref_s, 128, axis=1)
-    frac_exact = np.mean(gq[same] == ref_q[same])
+    # compare code values (0x00 and 0x80 are both zero)
+    gv, rv = F.decode_e4m3(gq), F.decode_e4m3(ref_q)
+    frac_exact = np.mean(gv[same] == rv[same])
     log("  exact h codes: %.5f" % frac_exact)
     assert frac_exact > 0.99
     # every GPU code is within one e4m3 step of the exact h
@@ -251,13 +257,14 @@ def test_gemm1_swiglu_parity(moe, cfg, over):
             _, _, fl = h_rounding_allowance(A[r0:r1], lay["w13"][e], lay["w13_s"][e], lay["w2"][e], lay["w2_s"][e])
             flag_el[r0:r1], flag_blk[r0:r1] = fl["element"], fl["block"]
     assert np.all(flag_blk[gs != ref_s])
-    differ = (gq != ref_q) & same
+    differ = (gv != rv) & same
     log("  differing codes: %d of %d, all flagged: %s (flagged %d)"
         % (differ.sum(), differ.size, bool(np.all(flag_el[differ])), flag_el.sum()))
     assert np.all(flag_el[differ])
 
 
-@pytest.mark.parametrize("T,H,I,E,k", [(64, 4096, 2048, 8, 8), (40, 1024, 640, 12, 3), (30, 6144, 256, 6, 4)])
+@pytest.mark.parametrize("T,H,I,E,k", [(64, 4096, 2048, 8, 8), (40, 1024, 640, 12, 3), (30, 6144, 256, 6, 4),
+                                       (300, 1024, 512, 8, 4), (100, 6144, 2048, 8, 8)])
 def test_gemm1_accumulation_error_bound(moe, T, H, I, E, k):
     """On random operands the float32 pre-activations are within ACC_REL * sum|a_k w_k| of
     the exact values: the premise of the rounding allowance of the output checks."""
