@@ -17,49 +17,82 @@
 // Streaming structure (weight-bandwidth-bound shapes): a workgroup owns one
 // m-tile of 16 rows of one expert and a block of weight rows; every weight
 // byte is read exactly once per m-tile, directly into registers, never
-// through LDS.  To make each lane's weight reads contiguous, K is walked in
-// super-steps of S*128: within a super-step, MFMA s pairs logical k-block b
-// (32 wide) with physical block S*b + s.  A lane then reads 16*S contiguous
-// weight bytes and S consecutive scale bytes (one dword for S = 4, selected
-// by op_sel = s), and the activation pieces are gathered to match.
+// through LDS.  K is walked in natural order, 128 per MFMA, S MFMAs per
+// pipeline stage: one load instruction then covers 64 contiguous bytes of each
+// of 16 weight rows (4 lanes per row).  Lane (g, r) needs the scale of 32-block
+// 4s + g at step s: it loads the row's 4S scale bytes of the stage and shifts
+// byte g of word s to the bottom (op_sel 0).  The activation scale of step s is
+// the row's scale byte of that 128-channel block.
 #include "moe_internal.h"
 
 namespace moe {
 
 template <int S>
 struct Stage {
-    uint4 w[4][S];      // weight codes, 4 row-tiles
-    uint32_t ws[4];     // weight scales (S bytes used)
-    uint4 xa[S], xb[S]; // activation halves
-    uint32_t xs;        // activation scale byte
+    uint4 w[4][S];      // weight codes, 4 row-tiles x S steps
+    uint32_t ws[4][S];  // weight scale words (byte g of word s used at step s)
+    v8i x[S];           // activation operand of each step (both 16-byte halves)
+    uint32_t xs[S];     // activation scale byte of each step
 };
 
 template <int S>
-__device__ __forceinline__ uint32_t load_scale_bytes(const uint8_t* p) {
-    if constexpr (S == 4) return *(const uint32_t*)p;
-    else if constexpr (S == 2) return *(const uint16_t*)p;
-    else return *p;
+__device__ __forceinline__ void load_scale_words(const uint8_t* p, uint32_t (&w)[S]) {
+    if constexpr (S == 4) {
+        const uint4 v = *(const uint4*)p;
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (S == 2) {
+        const uint2 v = *(const uint2*)p;
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        w[0] = *(const uint32_t*)p;
+    }
+}
+
+struct Ptrs {
+    const uint8_t* w[4];   // this lane's first weight byte of each row-tile
+    const uint8_t* s[4];   // first scale byte of each weight row
+    const uint8_t* x;      // this lane's first activation byte
+    const uint8_t* xs;     // first activation scale byte of the row
+};
+
+// one pipeline stage (S steps of 128 K) starting at K offset kk
+template <int S>
+__device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
+    Stage<S> st;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) st.w[j][s] = *(const uint4*)(P.w[j] + kk / 2 + 64 * s);
+        load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const uint4 lo = *(const uint4*)(P.x + kk + 128 * s);
+        const uint4 hi = *(const uint4*)(P.x + kk + 128 * s + 64);
+        st.x[s] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    // separate byte loads (a relaxed atomic load is never merged with its
+    // neighbour, which would need VALU extraction and an early wait)
+#pragma unroll
+    for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
+    return st;
 }
 
 template <int S, int s>
-__device__ __forceinline__ void mfma_step(const Stage<S>& st, v4f (&acc)[4]) {
-    v8i b;
-    b[0] = st.xa[s].x; b[1] = st.xa[s].y; b[2] = st.xa[s].z; b[3] = st.xa[s].w;
-    b[4] = st.xb[s].x; b[5] = st.xb[s].y; b[6] = st.xb[s].z; b[7] = st.xb[s].w;
+__device__ __forceinline__ void mfma_step(const Stage<S>& st, v4f (&acc)[4], int gshift) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        v8i a;
-        a[0] = st.w[j][s].x; a[1] = st.w[j][s].y; a[2] = st.w[j][s].z; a[3] = st.w[j][s].w;
-        a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
-        acc[j] = mfma_w4a8<s>(a, b, acc[j], (int)st.ws[j], (int)st.xs);
+        const uint4 w = st.w[j][s];
+        const v8i a = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+        acc[j] = mfma_w4a8<0, 0>(a, st.x[s], acc[j], (int)(st.ws[j][s] >> gshift), (int)st.xs[s]);
     }
 }
 
 template <int S>
-__device__ __forceinline__ void compute_stage(const Stage<S>& st, v4f (&acc)[4]) {
-    mfma_step<S, 0>(st, acc);
-    if constexpr (S > 1) mfma_step<S, 1>(st, acc);
-    if constexpr (S > 2) { mfma_step<S, 2>(st, acc); mfma_step<S, 3>(st, acc); }
+__device__ __forceinline__ void compute_stage(const Stage<S>& st, v4f (&acc)[4], int gshift) {
+    mfma_step<S, 0>(st, acc, gshift);
+    if constexpr (S > 1) mfma_step<S, 1>(st, acc, gshift);
+    if constexpr (S > 2) { mfma_step<S, 2>(st, acc, gshift); mfma_step<S, 3>(st, acc, gshift); }
 }
 
 template <int MODE, int S>
@@ -93,51 +126,44 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     }
 
     const size_t wstride = (size_t)K / 2, sstride = (size_t)K / 32;
-    const uint8_t* wp[4];
-    const uint8_t* sp[4];
+    Ptrs P;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const size_t row = (size_t)e * wrows + wrow[j] + r;
-        wp[j] = a.w + row * wstride + g * 16 * S;
-        sp[j] = a.w_scale + row * sstride + g * S;
+        P.w[j] = a.w + row * wstride + 16 * g;
+        P.s[j] = a.w_scale + row * sstride;
     }
+    const int gshift = 8 * g;
     const int arow = row0 + min(r, nrows - 1);
-    const uint8_t* xp = a.act + (size_t)arow * K;
-    const int xoff_a = 32 * (S * (g >> 1)) + 16 * (g & 1);
-    const int xoff_b = 32 * (S * (2 + (g >> 1))) + 16 * (g & 1);
-    const uint8_t* xsp = a.act_scale + (size_t)arow * (K / kFp8Block) + (S * g) / 4;
-
-    auto load = [&](Stage<S>& st, int kk) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int s = 0; s < S; ++s) st.w[j][s] = *(const uint4*)(wp[j] + kk / 2 + 16 * s);
-            st.ws[j] = load_scale_bytes<S>(sp[j] + kk / 32);
-        }
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            st.xa[s] = *(const uint4*)(xp + kk + xoff_a + 32 * s);
-            st.xb[s] = *(const uint4*)(xp + kk + xoff_b + 32 * s);
-        }
-        st.xs = xsp[kk / kFp8Block];
-    };
+    P.x = a.act + (size_t)arow * K + 16 * g;
+    P.xs = a.act_scale + (size_t)arow * (K / kFp8Block);
 
     v4f acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // software pipeline over two register stages, ping-pong without copies:
+    // while one stage is multiplied the other one's loads are in flight, and
+    // each wait covers only the stage about to be consumed.  Loads past the
+    // end re-read the last stage (an L2 hit) so that every load is unconditional.
+    // The scheduling barriers keep each phase's instructions in place, so the
+    // in-order load counter lets every wait cover exactly one stage.
     constexpr int KS = 128 * S;
-    const int nsteps = K / KS;
-    Stage<S> s0, s1;
-    load(s0, 0);
-    for (int i = 0; i < nsteps; i += 2) {
-        if (i + 1 < nsteps) load(s1, (i + 1) * KS);
-        compute_stage<S>(s0, acc);
-        if (i + 1 < nsteps) {
-            if (i + 2 < nsteps) load(s0, (i + 2) * KS);
-            compute_stage<S>(s1, acc);
-        }
+    const int klast = K - KS;
+    Stage<S> s0 = load_stage<S>(P, 0);
+    Stage<S> s1 = load_stage<S>(P, min(KS, klast));
+    int kk = 0;
+    for (; kk + 2 * KS <= K; kk += 2 * KS) {
+        compute_stage<S>(s0, acc, gshift);
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = load_stage<S>(P, min(kk + 2 * KS, klast));
+        __builtin_amdgcn_sched_barrier(0);
+        compute_stage<S>(s1, acc, gshift);
+        __builtin_amdgcn_sched_barrier(0);
+        s1 = load_stage<S>(P, min(kk + 3 * KS, klast));
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (kk < K) compute_stage<S>(s0, acc, gshift);   // odd number of stages: the last one is in s0
 
     // ---- epilogues ----
     const int orow = row0 + r;
@@ -192,9 +218,9 @@ static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     const int64_t tiles = (a.N + kRowsPerTile - 1) / kRowsPerTile + a.E;
     const int gx = (MODE == kGemm2) ? (a.H + 255) / 256 : a.I / 128;
     dim3 grid(gx, (unsigned)tiles), block(256);
-    if (K % 512 == 0)
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 4>), grid, block, 0, stream, a);
-    else if (K % 256 == 0)
+    // stages of 256 K (two MFMA steps), two stages in flight per wave: about
+    // 16 KB of weights in flight per wave, over 100 KB per CU
+    if (K % 256 == 0)
         hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2>), grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1>), grid, block, 0, stream, a);

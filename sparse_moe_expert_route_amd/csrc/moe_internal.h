@@ -51,9 +51,10 @@ __device__ __forceinline__ uint16_t float_to_bf16_rne(float f) {
 
 // Block-scaled MFMA, A = FP4 (e2m1) weights, B = FP8 (e4m3) activations:
 // D[16 weight rows][16 tokens] += sum_k A[row][k] * B[token][k] over 128 k.
-template <int OPSEL_A>
+// OPSEL_A / OPSEL_B pick the scale byte within each lane's scale register.
+template <int OPSEL_A, int OPSEL_B = 0>
 __device__ __forceinline__ v4f mfma_w4a8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, OPSEL_A, scale_a, 0, scale_b);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, OPSEL_A, scale_a, OPSEL_B, scale_b);
 }
 
 // ---------------------------------------------------------------------------
