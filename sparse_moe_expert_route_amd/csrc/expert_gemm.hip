@@ -53,17 +53,34 @@ struct Ptrs {
     const uint8_t* s[4];   // first scale byte of each weight row
     const uint8_t* x;      // this lane's first activation byte
     const uint8_t* xs;     // first activation scale byte of the row
+    uint32_t ls[4];        // LDS byte offset of each weight row's scales (scales staged in LDS)
+    uint32_t lx;           // LDS byte offset of the activation row's scales
 };
 
+// Scales staged in LDS: the workgroup's 256 weight rows, K/32 bytes each with
+// an 8-byte pad (rows 8-byte aligned; 16 consecutive rows hit distinct bank
+// pairs for K/32 in {64, 128, 192}), then its 16 activation rows, K/128 bytes
+// each with a 4-byte pad.
+extern __shared__ __attribute__((aligned(16))) uint8_t stream_smem[];
+__host__ __device__ constexpr int w_scale_pitch(int K) { return K / 32 + 8; }
+__host__ __device__ constexpr int x_scale_pitch(int K) { return K / 128 + 4; }
+__host__ __device__ constexpr int stream_lds_bytes(int K) { return 256 * w_scale_pitch(K) + 16 * x_scale_pitch(K); }
+
 // one pipeline stage (S steps of 128 K) starting at K offset kk
-template <int S>
+template <int S, bool SL>
 __device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
     Stage<S> st;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int s = 0; s < S; ++s) st.w[j][s] = *(const uint4*)(P.w[j] + kk / 2 + 64 * s);
-        load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
+        if constexpr (SL) {
+            static_assert(S == 2, "LDS-staged scales use two-step stages");
+            const uint2 v = *(const uint2*)(stream_smem + P.ls[j] + kk / 32);
+            st.ws[j][0] = v.x; st.ws[j][1] = v.y;
+        } else {
+            load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
+        }
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -71,31 +88,76 @@ __device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
         const uint4 hi = *(const uint4*)(P.x + kk + 128 * s + 64);
         st.x[s] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    // separate byte loads (a relaxed atomic load is never merged with its
-    // neighbour, which would need VALU extraction and an early wait)
+    if constexpr (SL) {
+        // both steps' scale bytes in one 16-bit LDS read; the MFMA picks byte s
+        st.xs[0] = *(const uint16_t*)(stream_smem + P.lx + kk / kFp8Block);
+    } else {
+        // separate byte loads (a relaxed atomic load is never merged with its
+        // neighbour, which would need VALU extraction and an early wait)
 #pragma unroll
-    for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
+        for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
+    }
     return st;
 }
 
-template <int S, int s>
+template <int S, bool SL, int s>
 __device__ __forceinline__ void mfma_step(const Stage<S>& st, v4f (&acc)[4], int gshift) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint4 w = st.w[j][s];
         const v8i a = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-        acc[j] = mfma_w4a8<0, 0>(a, st.x[s], acc[j], (int)(st.ws[j][s] >> gshift), (int)st.xs[s]);
+        if constexpr (SL)
+            acc[j] = mfma_w4a8<0, s>(a, st.x[s], acc[j], (int)(st.ws[j][s] >> gshift), (int)st.xs[0]);
+        else
+            acc[j] = mfma_w4a8<0, 0>(a, st.x[s], acc[j], (int)(st.ws[j][s] >> gshift), (int)st.xs[s]);
     }
 }
 
-template <int S>
+template <int S, bool SL>
 __device__ __forceinline__ void compute_stage(const Stage<S>& st, v4f (&acc)[4], int gshift) {
-    mfma_step<S, 0>(st, acc, gshift);
-    if constexpr (S > 1) mfma_step<S, 1>(st, acc, gshift);
-    if constexpr (S > 2) { mfma_step<S, 2>(st, acc, gshift); mfma_step<S, 3>(st, acc, gshift); }
+    mfma_step<S, SL, 0>(st, acc, gshift);
+    if constexpr (S > 1) mfma_step<S, SL, 1>(st, acc, gshift);
+    if constexpr (S > 2) { mfma_step<S, SL, 2>(st, acc, gshift); mfma_step<S, SL, 3>(st, acc, gshift); }
 }
 
-template <int MODE, int S>
+// Stage the workgroup's weight scales (256 rows) and activation scales (16
+// rows, clamped to the m-tile's last real row) in LDS: coalesced 16-byte
+// loads, issued together, then one wait.  K % 512 == 0, K <= 7680.
+template <int MODE>
+__device__ __forceinline__ void stage_scales(const GemmArgs& a, int e, int K, int row0, int nrows) {
+    const int tid = threadIdx.x;
+    const int SB = K / 32, WP = w_scale_pitch(K), n16 = SB / 16;   // 16-byte pieces per weight row
+    const int wrows = (MODE == kGemm2) ? a.H : 2 * a.I;
+    const uint8_t* base = a.w_scale + (size_t)e * wrows * SB;
+    uint4 v[15] = {};
+#pragma unroll
+    for (int q = 0; q < 15; ++q) {
+        if (q < n16) {
+            const int i = tid + 256 * q, R = i / n16, c = i - R * n16;
+            int grow;
+            if constexpr (MODE == kGemm2) grow = blockIdx.x * 256 + R;
+            else grow = (R < 128 ? 0 : a.I - 128) + blockIdx.x * 128 + R;
+            if (grow < wrows) v[q] = *(const uint4*)(base + (size_t)grow * SB + 16 * c);
+        }
+    }
+    const int XB = K / kFp8Block, n4 = XB / 4;                       // dwords per activation row
+    uint32_t xv = 0;
+    const int xr = tid / n4, xc = tid - xr * n4;
+    if (xr < 16) xv = *(const uint32_t*)(a.act_scale + (size_t)(row0 + min(xr, nrows - 1)) * XB + 4 * xc);
+#pragma unroll
+    for (int q = 0; q < 15; ++q) {
+        if (q < n16) {
+            const int i = tid + 256 * q, R = i / n16, c = i - R * n16;
+            uint8_t* d = stream_smem + R * WP + 16 * c;
+            *(uint2*)d = uint2{v[q].x, v[q].y};
+            *(uint2*)(d + 8) = uint2{v[q].z, v[q].w};
+        }
+    }
+    if (xr < 16) *(uint32_t*)(stream_smem + 256 * WP + xr * x_scale_pitch(K) + 4 * xc) = xv;
+    __syncthreads();
+}
+
+template <int MODE, int S, bool SL>
 __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
@@ -117,10 +179,12 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     int wrow[4];
     if constexpr (MODE == kGemm2) {
         const int n0 = blockIdx.x * 256 + wave * 64;
-        if (n0 >= a.H) return;   // whole wave past the last output feature (no barriers in this mode)
+        if constexpr (SL) stage_scales<MODE>(a, e, K, row0, nrows);   // before any wave leaves
+        if (n0 >= a.H) return;   // whole wave past the last output feature (no later barrier in this mode)
 #pragma unroll
         for (int j = 0; j < 4; ++j) wrow[j] = n0 + 16 * j;
     } else {
+        if constexpr (SL) stage_scales<MODE>(a, e, K, row0, nrows);
         const int f0 = blockIdx.x * 128 + wave * 32;
         wrow[0] = f0; wrow[1] = f0 + 16; wrow[2] = a.I + f0; wrow[3] = a.I + f0 + 16;
     }
@@ -137,6 +201,15 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     const int arow = row0 + min(r, nrows - 1);
     P.x = a.act + (size_t)arow * K + 16 * g;
     P.xs = a.act_scale + (size_t)arow * (K / kFp8Block);
+    if constexpr (SL) {
+        // LDS row of tile j: the wave's 64 rows in the order the scales were staged
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int lrow = (MODE == kGemm2) ? 64 * wave + 16 * j : (j >> 1) * 128 + 32 * wave + 16 * (j & 1);
+            P.ls[j] = (uint32_t)((lrow + r) * w_scale_pitch(K));
+        }
+        P.lx = (uint32_t)(256 * w_scale_pitch(K) + r * x_scale_pitch(K));
+    }
 
     v4f acc[4];
 #pragma unroll
@@ -150,20 +223,20 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     // in-order load counter lets every wait cover exactly one stage.
     constexpr int KS = 128 * S;
     const int klast = K - KS;
-    Stage<S> s0 = load_stage<S>(P, 0);
-    Stage<S> s1 = load_stage<S>(P, min(KS, klast));
+    Stage<S> s0 = load_stage<S, SL>(P, 0);
+    Stage<S> s1 = load_stage<S, SL>(P, min(KS, klast));
     int kk = 0;
     for (; kk + 2 * KS <= K; kk += 2 * KS) {
-        compute_stage<S>(s0, acc, gshift);
+        compute_stage<S, SL>(s0, acc, gshift);
         __builtin_amdgcn_sched_barrier(0);
-        s0 = load_stage<S>(P, min(kk + 2 * KS, klast));
+        s0 = load_stage<S, SL>(P, min(kk + 2 * KS, klast));
         __builtin_amdgcn_sched_barrier(0);
-        compute_stage<S>(s1, acc, gshift);
+        compute_stage<S, SL>(s1, acc, gshift);
         __builtin_amdgcn_sched_barrier(0);
-        s1 = load_stage<S>(P, min(kk + 3 * KS, klast));
+        s1 = load_stage<S, SL>(P, min(kk + 3 * KS, klast));
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (kk < K) compute_stage<S>(s0, acc, gshift);   // odd number of stages: the last one is in s0
+    if (kk < K) compute_stage<S, SL>(s0, acc, gshift);   // odd number of stages: the last one is in s0
 
     // ---- epilogues ----
     const int orow = row0 + r;
@@ -220,10 +293,14 @@ static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     dim3 grid(gx, (unsigned)tiles), block(256);
     // stages of 256 K (two MFMA steps), two stages in flight per wave: about
     // 16 KB of weights in flight per wave, over 100 KB per CU
-    if (K % 256 == 0)
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2>), grid, block, 0, stream, a);
+    // Scales are staged in LDS once per workgroup where they fit: per-stage
+    // scale loads would cost as many memory requests as the weights.
+    if (K % 512 == 0 && stream_lds_bytes(K) <= 65536)
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, true>), grid, block, stream_lds_bytes(K), stream, a);
+    else if (K % 256 == 0)
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, false>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

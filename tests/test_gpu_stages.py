@@ -156,7 +156,8 @@ def _offsets_for(T, E, k, seed, skew=None):
 @pytest.mark.parametrize("T,H,I,E,k,skew", [(64, 256, 128, 8, 2, None), (40, 512, 256, 16, 4, 3.0),
                                             (9, 4096, 2048, 8, 8, None), (150, 1024, 384, 12, 3, 2.0),
                                             (3, 6144, 256, 4, 2, None), (300, 512, 512, 8, 4, 2.0),
-                                            (200, 1024, 256, 16, 8, None), (700, 256, 768, 8, 2, 6.0)])
+                                            (200, 1024, 256, 16, 8, None), (700, 256, 768, 8, 2, 6.0),
+                                            (5, 8192, 256, 4, 2, None)])
 def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
     log("gemm1 lossless T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
     N = T * k
@@ -179,7 +180,8 @@ def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 8, 2), (40, 512, 256, 16, 4), (9, 4096, 2048, 8, 8),
-                                       (33, 384, 640, 5, 2), (300, 512, 512, 8, 4), (200, 1280, 256, 16, 8)])
+                                       (33, 384, 640, 5, 2), (300, 512, 512, 8, 4), (200, 1280, 256, 16, 8),
+                                       (50, 384, 512, 6, 2)])
 def test_gemm2_lossless_bitexact(moe, T, H, I, E, k):
     log("gemm2 lossless T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
     N = T * k
