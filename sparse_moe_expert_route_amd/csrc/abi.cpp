@@ -19,7 +19,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-    size_t logits, ids, w, offsets, sorted_token, row_of_slot, block_counts, block_base, tile_start;
+    size_t logits, ids, w, offsets, sorted_token, row_of_slot, block_counts, block_base, tile_start, tile_info;
     size_t xq, xs, hq, hs, y_perm, total;
 };
 
@@ -51,6 +51,7 @@ Layout layout_of(const moe_problem& p) {
     L.block_counts = take(nblk * E * 4);
     L.block_base = take(nblk * E * 4);
     L.tile_start = take((E + 1) * 4);
+    L.tile_info = take((size_t)max_tiles((int64_t)N, (int)E, kRowsPerTile) * 16);   // bound for both tile sizes
     L.xq = take(N * H);
     L.xs = take(N * (H / kFp8Block));
     L.hq = take(N * I);
@@ -116,10 +117,10 @@ moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, 
 }
 
 GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_scale, const int32_t* offsets,
-                   const int32_t* tile_start, const uint8_t* w, const uint8_t* w_scale, void* out,
+                   const int32_t* tile_start, const int4* tile_info, const uint8_t* w, const uint8_t* w_scale, void* out,
                    uint8_t* out_scale) {
     GemmArgs a;
-    a.act = act; a.act_scale = act_scale; a.offsets = offsets; a.tile_start = tile_start;
+    a.act = act; a.act_scale = act_scale; a.offsets = offsets; a.tile_start = tile_start; a.tile_info = tile_info;
     a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = out_scale;
     a.N = p.num_tokens * p.top_k;
     a.H = p.hidden; a.I = p.intermediate; a.E = p.num_experts;
@@ -144,18 +145,24 @@ moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, con
                      void* ws, bool plan, hipStream_t stream) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
+    int4* ti = at<int4>(ws, L.tile_info);
     const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
-    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, rpt, stream));
-    return launch_gemm(p, mode, gemm_args(p, xq, xs, offsets, ts, wt.w13, wt.w13_scale, out, out_scale), stream);
+    if (plan)
+        MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
+                                    max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
+    return launch_gemm(p, mode, gemm_args(p, xq, xs, offsets, ts, ti, wt.w13, wt.w13_scale, out, out_scale), stream);
 }
 
 moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const uint8_t* hs, const int32_t* offsets,
                      const moe_expert_weights& wt, float* y_perm, void* ws, bool plan, hipStream_t stream) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
+    int4* ti = at<int4>(ws, L.tile_info);
     const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
-    if (plan) MOE_LAUNCH(launch_tile_plan(offsets, ts, p.num_experts, rpt, stream));
-    return launch_gemm(p, kGemm2, gemm_args(p, hq, hs, offsets, ts, wt.w2, wt.w2_scale, y_perm, nullptr), stream);
+    if (plan)
+        MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
+                                    max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
+    return launch_gemm(p, kGemm2, gemm_args(p, hq, hs, offsets, ts, ti, wt.w2, wt.w2_scale, y_perm, nullptr), stream);
 }
 
 }  // namespace

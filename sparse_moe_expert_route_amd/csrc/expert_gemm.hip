@@ -57,30 +57,25 @@ struct Ptrs {
     uint32_t lx;           // LDS byte offset of the activation row's scales
 };
 
-// Scales staged in LDS: the workgroup's 256 weight rows, K/32 bytes each with
-// an 8-byte pad (rows 8-byte aligned; 16 consecutive rows hit distinct bank
-// pairs for K/32 in {64, 128, 192}), then its 16 activation rows, K/128 bytes
-// each with a 4-byte pad.
+// Scales staged in LDS: the workgroup's 256 weight rows (K/32 bytes each),
+// then its 16 activation rows (K/128 bytes each), unpadded, filled by direct
+// global->LDS loads.
 extern __shared__ __attribute__((aligned(16))) uint8_t stream_smem[];
-__host__ __device__ constexpr int w_scale_pitch(int K) { return K / 32 + 8; }
-__host__ __device__ constexpr int x_scale_pitch(int K) { return K / 128 + 4; }
-__host__ __device__ constexpr int stream_lds_bytes(int K) { return 256 * w_scale_pitch(K) + 16 * x_scale_pitch(K); }
+__host__ __device__ constexpr int stream_lds_bytes(int K) { return 256 * (K / 32) + 16 * (K / 128); }
 
-// one pipeline stage (S steps of 128 K) starting at K offset kk
-template <int S, bool SL>
-__device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
-    Stage<S> st;
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima)
+__host__ __device__ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// global loads of one pipeline stage (S steps of 128 K) at K offset kk:
+// 4*S weight loads and 2*S activation loads of 16 bytes per lane
+template <int S>
+__device__ __forceinline__ void load_stage_mem(const Ptrs& P, int kk, Stage<S>& st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int s = 0; s < S; ++s) st.w[j][s] = *(const uint4*)(P.w[j] + kk / 2 + 64 * s);
-        if constexpr (SL) {
-            static_assert(S == 2, "LDS-staged scales use two-step stages");
-            const uint2 v = *(const uint2*)(stream_smem + P.ls[j] + kk / 32);
-            st.ws[j][0] = v.x; st.ws[j][1] = v.y;
-        } else {
-            load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
-        }
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -88,15 +83,39 @@ __device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
         const uint4 hi = *(const uint4*)(P.x + kk + 128 * s + 64);
         st.x[s] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    if constexpr (SL) {
-        // both steps' scale bytes in one 16-bit LDS read; the MFMA picks byte s
-        st.xs[0] = *(const uint16_t*)(stream_smem + P.lx + kk / kFp8Block);
-    } else {
-        // separate byte loads (a relaxed atomic load is never merged with its
-        // neighbour, which would need VALU extraction and an early wait)
+}
+constexpr int kStageLoads = 6 * 2;   // load_stage_mem<2>
+
+// scales of the stage from LDS (two-step stages)
+template <int S>
+__device__ __forceinline__ void load_stage_lds(const Ptrs& P, int kk, Stage<S>& st) {
+    static_assert(S == 2, "LDS-staged scales use two-step stages");
 #pragma unroll
-        for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
+    for (int j = 0; j < 4; ++j) {
+        const uint2 v = *(const uint2*)(stream_smem + P.ls[j] + kk / 32);   // 8 scale bytes of the stage
+        st.ws[j][0] = v.x; st.ws[j][1] = v.y;
     }
+    // both steps' activation scale bytes in one 16-bit read; the MFMA picks byte s
+    st.xs[0] = *(const uint16_t*)(stream_smem + P.lx + kk / kFp8Block);
+}
+
+// scales of the stage from global memory
+template <int S>
+__device__ __forceinline__ void load_stage_gscales(const Ptrs& P, int kk, Stage<S>& st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
+    // separate byte loads (a relaxed atomic load is never merged with its
+    // neighbour, which would need VALU extraction and an early wait)
+#pragma unroll
+    for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
+}
+
+template <int S, bool SL>
+__device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
+    Stage<S> st;
+    load_stage_mem<S>(P, kk, st);
+    if constexpr (SL) load_stage_lds<S>(P, kk, st);
+    else load_stage_gscales<S>(P, kk, st);
     return st;
 }
 
@@ -120,41 +139,37 @@ __device__ __forceinline__ void compute_stage(const Stage<S>& st, v4f (&acc)[4],
     if constexpr (S > 2) { mfma_step<S, SL, 2>(st, acc, gshift); mfma_step<S, SL, 3>(st, acc, gshift); }
 }
 
-// Stage the workgroup's weight scales (256 rows) and activation scales (16
-// rows, clamped to the m-tile's last real row) in LDS: coalesced 16-byte
-// loads, issued together, then one wait.  K % 512 == 0, K <= 7680.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Start the copy of the workgroup's scales into LDS: weight rows in the order
+// of the waves' row-tiles (GEMM-1: 128 gate rows then the 128 matching up
+// rows; GEMM-2: 256 consecutive output rows), 16 bytes per lane, then the
+// activation rows of the m-tile (clamped to its last real row), 4 bytes per
+// lane.  Direct global->LDS loads: lane l of a load lands at base + size * l.
+// The caller waits on the load counter and barriers before reading.
+// Needs K % 512 == 0 and stream_lds_bytes(K) <= 64 KB (at most 15 weight and
+// 4 activation loads per wave).
 template <int MODE>
-__device__ __forceinline__ void stage_scales(const GemmArgs& a, int e, int K, int row0, int nrows) {
-    const int tid = threadIdx.x;
-    const int SB = K / 32, WP = w_scale_pitch(K), n16 = SB / 16;   // 16-byte pieces per weight row
+__device__ __forceinline__ void stage_scales_issue(const GemmArgs& a, int e, int K, int row0, int nrows) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int SB = K / 32, n16 = SB / 16;                   // 16-byte pieces per weight row
     const int wrows = (MODE == kGemm2) ? a.H : 2 * a.I;
     const uint8_t* base = a.w_scale + (size_t)e * wrows * SB;
-    uint4 v[15] = {};
-#pragma unroll
-    for (int q = 0; q < 15; ++q) {
-        if (q < n16) {
-            const int i = tid + 256 * q, R = i / n16, c = i - R * n16;
-            int grow;
-            if constexpr (MODE == kGemm2) grow = blockIdx.x * 256 + R;
-            else grow = (R < 128 ? 0 : a.I - 128) + blockIdx.x * 128 + R;
-            if (grow < wrows) v[q] = *(const uint4*)(base + (size_t)grow * SB + 16 * c);
-        }
+    for (int q = 0; q < n16; ++q) {
+        const int m = 4 * q + wave;                         // 1 KB piece of the LDS image
+        const int i = 64 * m + lane, R = i / n16, c = i - R * n16;
+        int grow;
+        if constexpr (MODE == kGemm2) grow = min((int)blockIdx.x * 256 + R, wrows - 1);   // rows past H: never read
+        else grow = (R < 128 ? 0 : a.I - 128) + blockIdx.x * 128 + R;
+        __builtin_amdgcn_global_load_lds(base + (size_t)grow * SB + 16 * c, (lds_void*)(stream_smem + 1024 * m), 16, 0, 0);
     }
-    const int XB = K / kFp8Block, n4 = XB / 4;                       // dwords per activation row
-    uint32_t xv = 0;
-    const int xr = tid / n4, xc = tid - xr * n4;
-    if (xr < 16) xv = *(const uint32_t*)(a.act_scale + (size_t)(row0 + min(xr, nrows - 1)) * XB + 4 * xc);
-#pragma unroll
-    for (int q = 0; q < 15; ++q) {
-        if (q < n16) {
-            const int i = tid + 256 * q, R = i / n16, c = i - R * n16;
-            uint8_t* d = stream_smem + R * WP + 16 * c;
-            *(uint2*)d = uint2{v[q].x, v[q].y};
-            *(uint2*)(d + 8) = uint2{v[q].z, v[q].w};
-        }
+    const int XB = K / kFp8Block, n4 = XB / 4;              // dwords per activation row, 16 rows
+    const int i = 64 * wave + lane;                         // 64 dwords per load, 16 * n4 in all
+    if (i < 16 * n4) {
+        const int rr = i / n4, c = i - rr * n4;
+        const uint8_t* src = a.act_scale + (size_t)(row0 + min(rr, nrows - 1)) * XB + 4 * c;
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(stream_smem + 256 * SB + 256 * wave), 4, 0, 0);
     }
-    if (xr < 16) *(uint32_t*)(stream_smem + 256 * WP + xr * x_scale_pitch(K) + 4 * xc) = xv;
-    __syncthreads();
 }
 
 template <int MODE, int S, bool SL>
@@ -162,29 +177,22 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
 
-    // ---- m-tile -> expert (largest e with tile_start[e] <= tile) ----
-    const int tile = blockIdx.y;
-    if (tile >= a.tile_start[a.E]) return;
-    int lo = 0, hi = a.E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int row0 = a.offsets[e] + (tile - a.tile_start[e]) * kRowsPerTile;
-    const int nrows = min(kRowsPerTile, a.offsets[e + 1] - row0);
+    // ---- m-tile: expert, first row, rows ----
+    const int4 ti = a.tile_info[blockIdx.y];
+    if (ti.x < 0) return;   // past the last m-tile
+    const int e = ti.x, row0 = ti.y, nrows = ti.z;
 
     const int K = (MODE == kGemm2) ? a.I : a.H;
     const int wrows = (MODE == kGemm2) ? a.H : 2 * a.I;   // weight rows per expert
     int wrow[4];
+    bool live = true;   // GEMM-2: false for a wave past the last output feature
     if constexpr (MODE == kGemm2) {
-        const int n0 = blockIdx.x * 256 + wave * 64;
-        if constexpr (SL) stage_scales<MODE>(a, e, K, row0, nrows);   // before any wave leaves
-        if (n0 >= a.H) return;   // whole wave past the last output feature (no later barrier in this mode)
+        int n0 = blockIdx.x * 256 + wave * 64;
+        live = n0 < a.H;
+        if (!live) n0 = a.H - 64;   // keeps its loads in bounds until it leaves after the barrier
 #pragma unroll
         for (int j = 0; j < 4; ++j) wrow[j] = n0 + 16 * j;
     } else {
-        if constexpr (SL) stage_scales<MODE>(a, e, K, row0, nrows);
         const int f0 = blockIdx.x * 128 + wave * 32;
         wrow[0] = f0; wrow[1] = f0 + 16; wrow[2] = a.I + f0; wrow[3] = a.I + f0 + 16;
     }
@@ -202,13 +210,13 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     P.x = a.act + (size_t)arow * K + 16 * g;
     P.xs = a.act_scale + (size_t)arow * (K / kFp8Block);
     if constexpr (SL) {
-        // LDS row of tile j: the wave's 64 rows in the order the scales were staged
+        // LDS row of tile j: the wave's 64 rows in the order the scales are staged
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int lrow = (MODE == kGemm2) ? 64 * wave + 16 * j : (j >> 1) * 128 + 32 * wave + 16 * (j & 1);
-            P.ls[j] = (uint32_t)((lrow + r) * w_scale_pitch(K));
+            P.ls[j] = (uint32_t)((lrow + r) * (K / 32));
         }
-        P.lx = (uint32_t)(256 * w_scale_pitch(K) + r * x_scale_pitch(K));
+        P.lx = (uint32_t)(256 * (K / 32) + r * (K / kFp8Block));
     }
 
     v4f acc[4];
@@ -223,8 +231,26 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     // in-order load counter lets every wait cover exactly one stage.
     constexpr int KS = 128 * S;
     const int klast = K - KS;
-    Stage<S> s0 = load_stage<S, SL>(P, 0);
-    Stage<S> s1 = load_stage<S, SL>(P, min(KS, klast));
+    Stage<S> s0, s1;
+    if constexpr (SL) {
+        // the scale copy overlaps the first two stages' weight and activation
+        // loads: wait for the copy alone (the load counter retires in order;
+        // the two stages issue kStageLoads loads each), then barrier
+        stage_scales_issue<MODE>(a, e, K, row0, nrows);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage_mem<S>(P, 0, s0);
+        load_stage_mem<S>(P, min(KS, klast), s1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kStageLoads));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (!live) return;
+        load_stage_lds<S>(P, 0, s0);
+        load_stage_lds<S>(P, min(KS, klast), s1);
+    } else {
+        s0 = load_stage<S, SL>(P, 0);
+        s1 = load_stage<S, SL>(P, min(KS, klast));
+    }
     int kk = 0;
     for (; kk + 2 * KS <= K; kk += 2 * KS) {
         compute_stage<S, SL>(s0, acc, gshift);
@@ -288,7 +314,7 @@ template <int MODE>
 static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     // grid.y: upper bound on m-tiles (sum over experts of ceil(n_e / 16));
     // workgroups past the real tile count exit at once.
-    const int64_t tiles = (a.N + kRowsPerTile - 1) / kRowsPerTile + a.E;
+    const int tiles = max_tiles(a.N, a.E, kRowsPerTile);
     const int gx = (MODE == kGemm2) ? (a.H + 255) / 256 : a.I / 128;
     dim3 grid(gx, (unsigned)tiles), block(256);
     // stages of 256 K (two MFMA steps), two stages in flight per wave: about

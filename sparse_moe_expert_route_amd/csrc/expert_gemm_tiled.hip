@@ -82,14 +82,8 @@ __global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
 
     for (int item = beg + (int)(blockIdx.x >> 3); item < end; item += per_xcd) {
         const int tile = item / NB, nblk = item - tile * NB;
-        int lo = 0, hi = a.E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-        }
-        const int e = lo;
-        const int row0 = a.offsets[e] + (tile - a.tile_start[e]) * kTileRows;
-        const int nrows = min(kTileRows, a.offsets[e + 1] - row0);
+        const int4 ti = a.tile_info[tile];
+        const int e = ti.x, row0 = ti.y, nrows = ti.z;
 
         // weight rows of this wave: two 32-row tiles
         int wrow0, wrow1;

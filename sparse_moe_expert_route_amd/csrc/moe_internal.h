@@ -76,8 +76,11 @@ hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, co
 hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq,
                                uint8_t* xs, int64_t N, int H, int64_t T, hipStream_t stream);
 
-hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int E, int rows_per_tile,
-                            hipStream_t stream);
+// tile_info[t] = {expert, first row, rows} of m-tile t for t < max_tiles
+// (expert -1 past the last tile); max_tiles = ceil(N / rows_per_tile) + E.
+hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, int E, int rows_per_tile,
+                            int max_tiles, hipStream_t stream);
+inline int max_tiles(int64_t N, int E, int rows_per_tile) { return (int)((N + rows_per_tile - 1) / rows_per_tile) + E; }
 
 enum GemmMode { kGemm1Swiglu = 0, kGemm1Preact = 1, kGemm2 = 2 };
 
@@ -89,6 +92,7 @@ struct GemmArgs {
     const uint8_t* act_scale;  // [N][K/128] e8m0
     const int32_t* offsets;    // [E+1]
     const int32_t* tile_start; // [E+1], tiles of kRowsPerTile rows
+    const int4* tile_info;     // per m-tile {expert, first row, rows}, expert -1 past the end
     const uint8_t* w;          // codes
     const uint8_t* w_scale;    // e8m0 per 32
     void* out;                 // swiglu: hq [N][I] + hs; preact: float [N][2I]; gemm2: float [N][H]

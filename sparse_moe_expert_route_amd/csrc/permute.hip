@@ -175,10 +175,14 @@ hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, u
 // [tile_start[e], tile_start[e+1]) of rows_per_tile rows each.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ tile_start, int E, int rpt) {
+                                                        int32_t* __restrict__ tile_start, int4* __restrict__ tile_info,
+                                                        int E, int rpt, int max_tiles) {
     __shared__ int tot[512];
+    __shared__ int start[513];
+    __shared__ int off[513];
     const int e = threadIdx.x;
-    const int n = (e < E) ? (offsets[e + 1] - offsets[e] + rpt - 1) / rpt : 0;
+    const int o0 = (e < E) ? offsets[e] : 0, o1 = (e < E) ? offsets[e + 1] : 0;
+    const int n = (e < E) ? (o1 - o0 + rpt - 1) / rpt : 0;
     tot[e] = n;
     __syncthreads();
     for (int d = 1; d < 512; d <<= 1) {
@@ -187,13 +191,29 @@ __global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restric
         tot[e] += v;
         __syncthreads();
     }
-    if (e < E) tile_start[e] = tot[e] - n;
-    if (e == E - 1) tile_start[E] = tot[e];
+    if (e < E) { start[e] = tot[e] - n; off[e] = o0; tile_start[e] = tot[e] - n; }
+    if (e == E - 1) { start[E] = tot[e]; off[E] = o1; tile_start[E] = tot[e]; }
+    __syncthreads();
+    const int ntiles = start[E];
+    for (int t = e; t < max_tiles; t += 512) {
+        int4 info = {-1, 0, 0, 0};
+        if (t < ntiles) {
+            int lo = 0, hi = E - 1;   // largest expert whose first tile is <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (start[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int row0 = off[lo] + (t - start[lo]) * rpt;
+            info = int4{lo, row0, min(rpt, off[lo + 1] - row0), 0};
+        }
+        tile_info[t] = info;
+    }
 }
 
-hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int E, int rows_per_tile,
-                            hipStream_t stream) {
-    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(512), 0, stream, offsets, tile_start, E, rows_per_tile);
+hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, int E, int rows_per_tile,
+                            int max_tiles, hipStream_t stream) {
+    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(512), 0, stream, offsets, tile_start, tile_info, E,
+                       rows_per_tile, max_tiles);
     return hipGetLastError();
 }
 
