@@ -29,6 +29,8 @@
 // together on the same L2.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -54,15 +56,210 @@ __device__ __forceinline__ v16f mfma32_w4a8(v8i a, v8i b, v16f c, int scale_a, i
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 0, OPSEL_A, scale_a, 0, scale_b);
 }
 
+// Activation stage ring in LDS: three buffers, declared as separate objects
+// so that the compiler's wait tracking for direct global->LDS loads can tell
+// a buffer being filled from the one being read.
+__shared__ __attribute__((aligned(16))) uint8_t tl_act0[kTileRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t tl_act1[kTileRows * kStageK];
+__shared__ __attribute__((aligned(16))) uint8_t tl_act2[kTileRows * kStageK];
+// activation scales: 2 bytes per row in dword slots; wave w's 32 rows at
+// slots 64w .. 64w+31 (its lanes 32..63 write a copy above them)
+__shared__ __attribute__((aligned(16))) uint32_t tl_scl0[2 * kTileRows];
+__shared__ __attribute__((aligned(16))) uint32_t tl_scl1[2 * kTileRows];
+__shared__ __attribute__((aligned(16))) uint32_t tl_scl2[2 * kTileRows];
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9
+// encoding, vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// vector-memory operations one stage issues per wave: 8 activation pieces,
+// 1 activation-scale piece, 8 weight loads, 2 weight-scale loads
+constexpr int kStageLoads = 19;
+
+// Workgroup barrier that waits on nothing: the callers first wait for their
+// own direct-to-LDS loads with an explicit vmcnt.  The empty asm statements
+// keep the compiler from moving memory accesses across it (a release fence
+// would also wait for every direct-to-LDS load in flight).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 struct WStage {
     uint4 w[2][4];    // 2 weight tiles x 4 steps of 16 bytes
     uint32_t ws[2];   // 4 scale bytes per tile
 };
 
+// Per-item state of the stage loop.
+struct TileCtx {
+    const uint8_t* act;        // FP8 activations [N][K]
+    const uint8_t* act_scale;  // [N][K/128]
+    const uint8_t* wp0;        // this lane's weight bytes, tile 0 (k = 0)
+    const uint8_t* wp1;        // tile 1
+    const uint8_t* sp0;        // this lane's weight scale bytes, tile 0
+    const uint8_t* sp1;        // tile 1
+    int K, nstage, row0, nrows;
+};
+
+// The K loop of one item.  The three activation buffers come in as restrict
+// pointers: the compiler then tags every LDS access with the buffer it
+// touches, and its wait tracking for direct global->LDS loads (which would
+// otherwise make each LDS read wait for every such load in flight) lets a
+// buffer be read while the others are being filled.
+__device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4][2],
+                                           uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
+                                           uint8_t* __restrict__ act2, uint32_t* __restrict__ scl0,
+                                           uint32_t* __restrict__ scl1, uint32_t* __restrict__ scl2) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, r = lane & 31;
+    const int K = c.K, nstage = c.nstage, row0 = c.row0, nrows = c.nrows;
+    const uint8_t* wp0 = c.wp0; const uint8_t* wp1 = c.wp1;
+    const uint8_t* sp0 = c.sp0; const uint8_t* sp1 = c.sp1;
+    auto abuf = [&](auto bc) -> uint8_t* {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (B == 0) return act0; else if constexpr (B == 1) return act1; else return act2;
+    };
+    auto sbuf = [&](auto bc) -> uint32_t* {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (B == 0) return scl0; else if constexpr (B == 1) return scl1; else return scl2;
+    };
+    auto load_w = [&](WStage& ws, int st) {
+        const int kb = st * (kStageK / 2);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            ws.w[0][s] = *(const uint4*)(wp0 + kb + 16 * s);
+            ws.w[1][s] = *(const uint4*)(wp1 + kb + 16 * s);
+        }
+        ws.ws[0] = *(const uint32_t*)(sp0 + st * (kStageK / 32));
+        ws.ws[1] = *(const uint32_t*)(sp1 + st * (kStageK / 32));
+    };
+
+    // activation stage: 128 rows x 256 bytes.  Wave w moves rows 32w .. 32w+31,
+    // four rows (64 lanes x 16 bytes) per instruction; lane i of an instruction
+    // fills chunk slot i%16 of row 4p + i/16 with the global chunk that the
+    // swizzle maps there.  Every wave also moves the two scale bytes of its
+    // rows (twice: all 64 lanes), so that every wave issues kStageLoads loads.
+    auto dma_act = [&](auto bufc, int st) {
+        constexpr int BUF = decltype(bufc)::value;
+        const int k0 = st * kStageK;
+        uint8_t* lds = abuf(bufc);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int row = 32 * wave + 4 * p + (lane >> 4);
+            const int chunk = (lane & 15) ^ (row & 15);
+            const int rr = row0 + min(row, nrows - 1);
+            dma16(c.act + (size_t)rr * K + k0 + 16 * chunk, lds + (32 * wave + 4 * p) * kStageK);
+        }
+        {
+            const int rr = row0 + min(32 * wave + (lane & 31), nrows - 1);
+            dma2(c.act_scale + (size_t)rr * (K / kFp8Block) + k0 / kFp8Block, sbuf(bufc) + 64 * wave);
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[j][t][i] = 0.0f;
+
+    // Three-deep pipeline: stage st+2's activations (into LDS) and weights
+    // (into a third register set) are issued while stage st is multiplied,
+    // so each load has two stages of MFMA work to land.  Buffer and
+    // register set of stage st are st mod 3; the stage loop is unrolled by
+    // three so that every set is a fixed set of registers.
+    WStage w0, w1, w2;
+    auto stage = [&](auto setc, int st, const WStage& wc, WStage& wn) {
+        constexpr int SET = decltype(setc)::value;
+        constexpr int NXT = (SET + 2) % 3;
+        // stage st landed (only stage st+1's loads may still be in flight),
+        // in every wave: then its buffer may be read, and the buffer of
+        // stage st-1, which stage st+2 refills, is no longer read.  Near
+        // the end the prefetch re-reads the last stage into a free buffer,
+        // so the body has no branch and the load count never changes.
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(kStageLoads));
+        lds_barrier();
+        dma_act(std::integral_constant<int, NXT>{}, min(st + 2, nstage - 1));
+        load_w(wn, min(st + 2, nstage - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* lds = abuf(setc);
+        int bs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bs[j] = (sbuf(setc)[64 * j + r] >> (8 * g)) & 0xFF;
+        // B operands one MFMA step ahead of their use
+        v8i B[2][4];
+        auto read_b = [&](v8i (&Bd)[4], int s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 32 * j + r;
+                const uint4 lo4 = *(const uint4*)(lds + swz(row, 2 * s + g));
+                const uint4 hi4 = *(const uint4*)(lds + swz(row, 8 + 2 * s + g));
+                Bd[j][0] = lo4.x; Bd[j][1] = lo4.y; Bd[j][2] = lo4.z; Bd[j][3] = lo4.w;
+                Bd[j][4] = hi4.x; Bd[j][5] = hi4.y; Bd[j][6] = hi4.z; Bd[j][7] = hi4.w;
+            }
+        };
+        read_b(B[0], 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) read_b(B[(s + 1) & 1], s + 1);
+            v8i A0, A1;
+            A0[0] = wc.w[0][s].x; A0[1] = wc.w[0][s].y; A0[2] = wc.w[0][s].z; A0[3] = wc.w[0][s].w;
+            A1[0] = wc.w[1][s].x; A1[1] = wc.w[1][s].y; A1[2] = wc.w[1][s].z; A1[3] = wc.w[1][s].w;
+            A0[4] = A0[5] = A0[6] = A0[7] = 0;
+            A1[4] = A1[5] = A1[6] = A1[7] = 0;
+            const v8i (&Bc)[4] = B[s & 1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                switch (s) {
+                    case 0:
+                        acc[j][0] = mfma32_w4a8<0>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
+                        acc[j][1] = mfma32_w4a8<0>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
+                        break;
+                    case 1:
+                        acc[j][0] = mfma32_w4a8<1>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
+                        acc[j][1] = mfma32_w4a8<1>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
+                        break;
+                    case 2:
+                        acc[j][0] = mfma32_w4a8<2>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
+                        acc[j][1] = mfma32_w4a8<2>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
+                        break;
+                    default:
+                        acc[j][0] = mfma32_w4a8<3>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
+                        acc[j][1] = mfma32_w4a8<3>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
+                        break;
+                }
+            }
+            // keep each step's LDS reads next to the step before their use
+            // (hoisting them all would need every B operand of the stage live)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    dma_act(I0{}, 0);
+    load_w(w0, 0);
+    dma_act(I1{}, min(1, nstage - 1));
+    load_w(w1, min(1, nstage - 1));
+    int st = 0;
+    for (; st + 3 <= nstage; st += 3) {
+        stage(I0{}, st, w0, w2);
+        stage(I1{}, st + 1, w1, w0);
+        stage(I2{}, st + 2, w2, w1);
+    }
+    if (st < nstage) stage(I0{}, st, w0, w2);
+    if (st + 1 < nstage) stage(I1{}, st + 1, w1, w0);
+    // the tail prefetches have landed and every wave is done reading the
+    // ring before the next item refills it
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    lds_barrier();
+
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t act_lds[2][kTileRows * kStageK];
-    __shared__ __attribute__((aligned(16))) uint32_t act_scale_lds[2][kTileRows];   // 2 scale bytes per row
     __shared__ float red[4][kTileRows];
 
     const int tid = threadIdx.x;
@@ -103,107 +300,12 @@ __global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
         const uint8_t* sp0 = a.w_scale + ((size_t)e * wrows + wrow0 + r) * sstride + 4 * g;
         const uint8_t* sp1 = a.w_scale + ((size_t)e * wrows + wrow1 + r) * sstride + 4 * g;
 
-        auto load_w = [&](WStage& ws, int st) {
-            const int kb = st * (kStageK / 2);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                ws.w[0][s] = *(const uint4*)(wp0 + kb + 16 * s);
-                ws.w[1][s] = *(const uint4*)(wp1 + kb + 16 * s);
-            }
-            ws.ws[0] = *(const uint32_t*)(sp0 + st * (kStageK / 32));
-            ws.ws[1] = *(const uint32_t*)(sp1 + st * (kStageK / 32));
-        };
-
-        // activation stage: 128 rows x 256 bytes.  Wave w moves rows 32w .. 32w+31,
-        // four rows (64 lanes x 16 bytes) per instruction; lane i of an instruction
-        // fills chunk slot i%16 of row 4p + i/16 with the global chunk that the
-        // swizzle maps there.  Waves 0 and 1 also move the rows' two scale bytes.
-        auto dma_act = [&](int st, int buf) {
-            const int k0 = st * kStageK;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) {
-                const int row = 32 * wave + 4 * p + (lane >> 4);
-                const int chunk = (lane & 15) ^ (row & 15);
-                const int rr = row0 + min(row, nrows - 1);
-                dma16(a.act + (size_t)rr * K + k0 + 16 * chunk, &act_lds[buf][(32 * wave + 4 * p) * kStageK]);
-            }
-            if (wave < 2) {
-                const int rr = row0 + min(64 * wave + lane, nrows - 1);
-                dma2(a.act_scale + (size_t)rr * (K / kFp8Block) + k0 / kFp8Block, &act_scale_lds[buf][64 * wave]);
-            }
-        };
-
+        TileCtx c;
+        c.act = a.act; c.act_scale = a.act_scale;
+        c.wp0 = wp0; c.wp1 = wp1; c.sp0 = sp0; c.sp1 = sp1;
+        c.K = K; c.nstage = nstage; c.row0 = row0; c.nrows = nrows;
         v16f acc[4][2];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[j][t][i] = 0.0f;
-
-        WStage wcur, wnext;
-        dma_act(0, 0);
-        load_w(wcur, 0);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-
-        for (int st = 0; st < nstage; ++st) {
-            const int buf = st & 1;
-            const bool more = st + 1 < nstage;
-            // operands of this stage from LDS first, so the next stage's LDS writes
-            // are issued after every read of this buffer pair
-            const uint8_t* lds = act_lds[buf];
-            v8i B[4][4];
-            int bs[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 32 * j + r;
-                bs[j] = (act_scale_lds[buf][row] >> (8 * g)) & 0xFF;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint4 lo4 = *(const uint4*)(lds + swz(row, 2 * s + g));
-                    const uint4 hi4 = *(const uint4*)(lds + swz(row, 8 + 2 * s + g));
-                    B[j][s][0] = lo4.x; B[j][s][1] = lo4.y; B[j][s][2] = lo4.z; B[j][s][3] = lo4.w;
-                    B[j][s][4] = hi4.x; B[j][s][5] = hi4.y; B[j][s][6] = hi4.z; B[j][s][7] = hi4.w;
-                }
-            }
-            if (more) {
-                dma_act(st + 1, buf ^ 1);
-                load_w(wnext, st + 1);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                v8i A0, A1;
-                A0[0] = wcur.w[0][s].x; A0[1] = wcur.w[0][s].y; A0[2] = wcur.w[0][s].z; A0[3] = wcur.w[0][s].w;
-                A1[0] = wcur.w[1][s].x; A1[1] = wcur.w[1][s].y; A1[2] = wcur.w[1][s].z; A1[3] = wcur.w[1][s].w;
-                A0[4] = A0[5] = A0[6] = A0[7] = 0;
-                A1[4] = A1[5] = A1[6] = A1[7] = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    switch (s) {
-                        case 0:
-                            acc[j][0] = mfma32_w4a8<0>(A0, B[j][s], acc[j][0], (int)wcur.ws[0], bs[j]);
-                            acc[j][1] = mfma32_w4a8<0>(A1, B[j][s], acc[j][1], (int)wcur.ws[1], bs[j]);
-                            break;
-                        case 1:
-                            acc[j][0] = mfma32_w4a8<1>(A0, B[j][s], acc[j][0], (int)wcur.ws[0], bs[j]);
-                            acc[j][1] = mfma32_w4a8<1>(A1, B[j][s], acc[j][1], (int)wcur.ws[1], bs[j]);
-                            break;
-                        case 2:
-                            acc[j][0] = mfma32_w4a8<2>(A0, B[j][s], acc[j][0], (int)wcur.ws[0], bs[j]);
-                            acc[j][1] = mfma32_w4a8<2>(A1, B[j][s], acc[j][1], (int)wcur.ws[1], bs[j]);
-                            break;
-                        default:
-                            acc[j][0] = mfma32_w4a8<3>(A0, B[j][s], acc[j][0], (int)wcur.ws[0], bs[j]);
-                            acc[j][1] = mfma32_w4a8<3>(A1, B[j][s], acc[j][1], (int)wcur.ws[1], bs[j]);
-                            break;
-                    }
-                }
-            }
-            if (more) wcur = wnext;
-            __builtin_amdgcn_s_waitcnt(0);   // this wave's LDS writes for the next stage have landed
-            __syncthreads();
-        }
+        tile_kloop(c, acc, tl_act0, tl_act1, tl_act2, tl_scl0, tl_scl1, tl_scl2);
 
         // ---- epilogues: lane holds tokens 32j + r, features 8*(i/4) + 4g + (i%4) of each tile ----
         if constexpr (MODE == kGemm2) {
