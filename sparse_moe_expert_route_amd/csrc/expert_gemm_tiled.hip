@@ -24,9 +24,11 @@
 // 16-byte chunk c of row p stored at chunk slot c ^ (p mod 16) so that the 32
 // rows read by one MFMA operand fetch hit distinct banks; every wave streams
 // its own weight rows straight into registers.  The grid is persistent: workgroups on one XCD
-// (block id mod 8) take a contiguous 1/8 of the item list, n-block fastest,
-// so items sharing an m-tile (activations) or an expert (weights) run
-// together on the same L2.
+// (block id mod 8) take a contiguous 1/8 of the item list.  Items are grouped
+// by expert; an expert's m-tiles go in chunks of four, each chunk ordered
+// n-block major, m-tile minor: the m-tiles that read the same block of weight
+// rows run side by side on one L2 (weights come from HBM about once per
+// chunk), and the chunk's activations stay in L2 across its n-blocks.
 #include "moe_internal.h"
 
 #include <type_traits>
@@ -37,6 +39,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTileRows = 128;            // m-tile rows
 constexpr int kStageK = 256;              // K per LDS stage (bytes of an FP8 row)
+constexpr int kMChunk = 4;                // m-tiles of one expert scheduled together
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -141,7 +144,6 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4][2],
     // swizzle maps there.  Every wave also moves the two scale bytes of its
     // rows (twice: all 64 lanes), so that every wave issues kStageLoads loads.
     auto dma_act = [&](auto bufc, int st) {
-        constexpr int BUF = decltype(bufc)::value;
         const int k0 = st * kStageK;
         uint8_t* lds = abuf(bufc);
 #pragma unroll
@@ -278,9 +280,20 @@ __global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
     const int end = (int)(((long long)total * (xcd + 1)) >> 3);
 
     for (int item = beg + (int)(blockIdx.x >> 3); item < end; item += per_xcd) {
-        const int tile = item / NB, nblk = item - tile * NB;
-        const int4 ti = a.tile_info[tile];
-        const int e = ti.x, row0 = ti.y, nrows = ti.z;
+        // items of expert e: [NB * tile_start[e], NB * tile_start[e+1]).  Its
+        // m-tiles go in chunks of kMChunk; within a chunk the order is n-block
+        // major, m-tile minor, so the m-tiles that share a block of weight rows
+        // run together, while a chunk's activations stay in L2 across n-blocks.
+        const int e = a.tile_info[item / NB].x;
+        const int t0 = a.tile_start[e], nt = a.tile_start[e + 1] - t0;
+        const int local = item - NB * t0;
+        const int full = nt / kMChunk;                              // full chunks
+        const int chunk = min(local / (kMChunk * NB), full);
+        const int cs = (chunk < full) ? kMChunk : nt - kMChunk * full;  // tiles in this chunk
+        const int within = local - kMChunk * NB * chunk;
+        const int nblk = within / cs;
+        const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
+        const int row0 = ti.y, nrows = ti.z;
 
         // weight rows of this wave: two 32-row tiles
         int wrow0, wrow1;
