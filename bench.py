@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens for the CPU oracle (0 = auto)")
+    ap.add_argument("--canonical-weights", action="store_true",
+                    help="run on the canonical (row-major) weight layout instead of the packed one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB copy kernel (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -78,6 +80,19 @@ def main():
     bias = None if lay["bias"] is None else dev(lay["bias"])
     W = moe.ExpertWeights(dev(lay["w13"]), dev(lay["w13_s"]), dev(lay["w2"]), dev(lay["w2_s"]))
     p = moe.Problem.make(T, H, inter, E, k)
+    prepack_ms = None
+    if not args.canonical_weights:
+        # one-time reordering of the expert code bytes at load time (untimed; reported)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        Wp = moe.prepack_weights(p, W)
+        e1.record()
+        torch.cuda.synchronize()
+        prepack_ms = e0.elapsed_time(e1)
+        del W
+        W = Wp
+        log("bench: prepacked expert weights in %.2f ms" % prepack_ms)
     ws = moe.alloc_workspace(p)
     y = torch.empty(T, H, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
@@ -141,7 +156,9 @@ def main():
         achieved = gemm1_flops / (gemm1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "expert_gemm_stream_kernel<gate/up + SwiGLU + FP8 requant>"
+    tiled = N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= 6144
+    roof["kernel"] = ("expert_gemm_tiled_kernel" if tiled else "expert_gemm_stream_kernel") + \
+        "<gate/up + SwiGLU + FP8 requant>"
     roof["launch_ms"] = round(gemm1_ms, 4)
     roof["algorithmic_bytes"] = int(gemm1_bytes)
     roof["algorithmic_flops"] = gemm1_flops
@@ -162,7 +179,9 @@ def main():
            "data": "synthetic (seeded; N(0,1) bf16 activations, 0.02*N(0,1) bf16 router and MXFP4 experts)",
            "config": {"workload": args.config, "T": T, "H": H, "E": E, "k": k, "I": inter, "seed": args.seed,
                       "bias": cfg["bias"]},
-           "roofline": roof, "layer": layer}
+           "roofline": roof, "layer": layer,
+           "weight_layout": "canonical" if args.canonical_weights else "packed",
+           "prepack_ms": None if prepack_ms is None else round(prepack_ms, 3)}
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(lay, args, T)

@@ -6,9 +6,9 @@ checks tensor dtypes/shapes, passes device pointers and torch's current HIP
 stream to the library, and turns status codes into exceptions.  There is no
 fallback: if the library is missing, every call raises.
 
-Names follow the C ABI: ``route``, ``permute``, ``grouped_gemm_swiglu``,
-``grouped_gemm1_swiglu``, ``grouped_gemm1_preact``, ``grouped_gemm2``,
-``combine``, ``forward``.
+Names follow the C ABI: ``prepack_weights``, ``route``, ``permute``,
+``grouped_gemm_swiglu``, ``grouped_gemm1_swiglu``, ``grouped_gemm1_preact``,
+``grouped_gemm2``, ``combine``, ``forward``.
 """
 
 import ctypes
@@ -18,9 +18,9 @@ import torch
 
 __all__ = [
     "MoeError", "Problem", "ExpertWeights", "lib_path", "load", "abi_version", "workspace_size",
-    "alloc_workspace", "route", "permute", "grouped_gemm_swiglu", "grouped_gemm1_swiglu",
+    "alloc_workspace", "prepack_weights", "route", "permute", "grouped_gemm_swiglu", "grouped_gemm1_swiglu",
     "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "OUT_F32", "OUT_BF16",
-    "EXPORTED_SYMBOLS",
+    "WEIGHTS_CANONICAL", "WEIGHTS_PACKED", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,9 +28,11 @@ lib_path = os.path.join(_HERE, "libmoe_mi355x.so")
 
 OUT_F32 = 0
 OUT_BF16 = 1
+WEIGHTS_CANONICAL = 0
+WEIGHTS_PACKED = 1
 
 EXPORTED_SYMBOLS = [
-    "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_route", "moe_permute",
+    "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_prepack_weights", "moe_route", "moe_permute",
     "moe_grouped_gemm_swiglu", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_preact",
     "moe_grouped_gemm2", "moe_combine", "moe_forward",
 ]
@@ -58,15 +60,18 @@ class Problem(ctypes.Structure):
 
 class _Weights(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p),
-                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+                ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 class ExpertWeights:
     """Device tensors of the MXFP4 experts (uint8):
-    w13 [E, 2I, H/2], w13_scale [E, 2I, H/32], w2 [E, H, I/2], w2_scale [E, H, I/32]."""
+    w13 [E, 2I, H/2], w13_scale [E, 2I, H/32], w2 [E, H, I/2], w2_scale [E, H, I/32].
+    ``layout`` says how the code bytes of w13 and w2 are ordered: WEIGHTS_CANONICAL
+    (row-major) or WEIGHTS_PACKED (as written by ``prepack_weights``; same shapes)."""
 
-    def __init__(self, w13, w13_scale, w2, w2_scale):
+    def __init__(self, w13, w13_scale, w2, w2_scale, layout=WEIGHTS_CANONICAL):
         self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
+        self.layout = int(layout)
 
     def check(self, p):
         E, H, I = p.num_experts, p.hidden, p.intermediate
@@ -77,7 +82,7 @@ class ExpertWeights:
 
     def struct(self):
         return _Weights(self.w13.data_ptr(), self.w13_scale.data_ptr(),
-                        self.w2.data_ptr(), self.w2_scale.data_ptr())
+                        self.w2.data_ptr(), self.w2_scale.data_ptr(), self.layout)
 
 
 _lib = None
@@ -100,6 +105,7 @@ def load():
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_workspace_size.restype = sz
     L.moe_workspace_size.argtypes = [P]
+    L.moe_prepack_weights.argtypes = [P, W, vp, vp, vp]
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_grouped_gemm_swiglu.argtypes = [P, vp, vp, vp, W, vp, vp, sz, vp]
@@ -155,6 +161,25 @@ def workspace_size(p):
 
 def alloc_workspace(p, device="cuda"):
     return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def prepack_weights(p, weights, w13_packed=None, w2_packed=None, stream=None):
+    """Reorder canonical expert codes into the packed layout; returns packed ExpertWeights
+    sharing the scale tensors.  Output tensors are allocated unless given."""
+    if weights.layout != WEIGHTS_CANONICAL:
+        raise ValueError("prepack_weights needs canonical weights")
+    weights.check(p)
+    if w13_packed is None:
+        w13_packed = torch.empty_like(weights.w13)
+    if w2_packed is None:
+        w2_packed = torch.empty_like(weights.w2)
+    _check(w13_packed, torch.uint8, tuple(weights.w13.shape), "w13_packed")
+    _check(w2_packed, torch.uint8, tuple(weights.w2.shape), "w2_packed")
+    W = weights.struct()
+    st = load().moe_prepack_weights(ctypes.byref(p), ctypes.byref(W), _ptr(w13_packed), _ptr(w2_packed),
+                                    _stream(stream))
+    _raise("moe_prepack_weights", st)
+    return ExpertWeights(w13_packed, weights.w13_scale, w2_packed, weights.w2_scale, WEIGHTS_PACKED)
 
 
 def route(p, x, w_router, sel_bias, logits, topk_ids, topk_w, stream=None):

@@ -75,7 +75,13 @@ moe_status check_weights(const moe_expert_weights* w) {
     if (!w || !w->w13 || !w->w13_scale || !w->w2 || !w->w2_scale) return MOE_ERR_INVALID_ARGUMENT;
     if (!aligned16(w->w13) || !aligned16(w->w13_scale) || !aligned16(w->w2) || !aligned16(w->w2_scale))
         return MOE_ERR_INVALID_ARGUMENT;
+    if (w->layout != MOE_WEIGHTS_CANONICAL && w->layout != MOE_WEIGHTS_PACKED) return MOE_ERR_INVALID_ARGUMENT;
     return MOE_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
 }
 
 #define MOE_CHECK(expr)                          \
@@ -122,6 +128,7 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_
     GemmArgs a;
     a.act = act; a.act_scale = act_scale; a.offsets = offsets; a.tile_start = tile_start; a.tile_info = tile_info;
     a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = out_scale;
+    a.packed = 0;
     a.N = p.num_tokens * p.top_k;
     a.H = p.hidden; a.I = p.intermediate; a.E = p.num_experts;
     return a;
@@ -150,7 +157,9 @@ moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, con
     if (plan)
         MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
                                     max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
-    return launch_gemm(p, mode, gemm_args(p, xq, xs, offsets, ts, ti, wt.w13, wt.w13_scale, out, out_scale), stream);
+    GemmArgs a = gemm_args(p, xq, xs, offsets, ts, ti, wt.w13, wt.w13_scale, out, out_scale);
+    a.packed = wt.layout == MOE_WEIGHTS_PACKED;
+    return launch_gemm(p, mode, a, stream);
 }
 
 moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const uint8_t* hs, const int32_t* offsets,
@@ -162,7 +171,9 @@ moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const uint8_t* hs,
     if (plan)
         MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
                                     max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
-    return launch_gemm(p, kGemm2, gemm_args(p, hq, hs, offsets, ts, ti, wt.w2, wt.w2_scale, y_perm, nullptr), stream);
+    GemmArgs a = gemm_args(p, hq, hs, offsets, ts, ti, wt.w2, wt.w2_scale, y_perm, nullptr);
+    a.packed = wt.layout == MOE_WEIGHTS_PACKED;
+    return launch_gemm(p, kGemm2, a, stream);
 }
 
 }  // namespace
@@ -185,6 +196,23 @@ const char* moe_status_string(moe_status s) {
 size_t moe_workspace_size(const moe_problem* p) {
     if (check_problem(p) != MOE_OK) return 0;
     return layout_of(*p).total;
+}
+
+moe_status moe_prepack_weights(const moe_problem* p, const moe_expert_weights* weights, uint8_t* w13_packed,
+                               uint8_t* w2_packed, hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (weights->layout != MOE_WEIGHTS_CANONICAL) return MOE_ERR_INVALID_ARGUMENT;
+    if (!all_aligned(w13_packed, w2_packed)) return MOE_ERR_INVALID_ARGUMENT;
+    const size_t E = (size_t)p->num_experts, H = (size_t)p->hidden, I = (size_t)p->intermediate;
+    const size_t n13 = E * 2 * I * (H / 2), n2 = E * H * (I / 2);
+    if (overlaps(w13_packed, n13, weights->w13, n13) || overlaps(w13_packed, n13, weights->w2, n2) ||
+        overlaps(w2_packed, n2, weights->w13, n13) || overlaps(w2_packed, n2, weights->w2, n2) ||
+        overlaps(w13_packed, n13, w2_packed, n2))
+        return MOE_ERR_INVALID_ARGUMENT;
+    MOE_LAUNCH(launch_prepack(weights->w13, w13_packed, (int64_t)(E * 2 * I), (int)H, stream));
+    MOE_LAUNCH(launch_prepack(weights->w2, w2_packed, (int64_t)(E * H), (int)I, stream));
+    return MOE_OK;
 }
 
 moe_status moe_route(const moe_problem* p, const void* x_bf16, const void* w_router_bf16, const float* sel_bias,

@@ -70,12 +70,17 @@ __host__ __device__ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4
 
 // global loads of one pipeline stage (S steps of 128 K) at K offset kk:
 // 4*S weight loads and 2*S activation loads of 16 bytes per lane
-template <int S>
+template <int S, bool PK>
 __device__ __forceinline__ void load_stage_mem(const Ptrs& P, int kk, Stage<S>& st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) st.w[j][s] = *(const uint4*)(P.w[j] + kk / 2 + 64 * s);
+        for (int s = 0; s < S; ++s) {
+            // canonical: 64 bytes of the row per step; packed: one 1 KB block
+            // (16 rows x 64 bytes) per step, lane l at 16 l
+            if constexpr (PK) st.w[j][s] = *(const uint4*)(P.w[j] + 8 * kk + 1024 * s);
+            else st.w[j][s] = *(const uint4*)(P.w[j] + kk / 2 + 64 * s);
+        }
     }
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -84,7 +89,7 @@ __device__ __forceinline__ void load_stage_mem(const Ptrs& P, int kk, Stage<S>& 
         st.x[s] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 }
-constexpr int kStageLoads = 6 * 2;   // load_stage_mem<2>
+constexpr int kStageLoads = 6 * 2;   // load_stage_mem<2, *>
 
 // scales of the stage from LDS (two-step stages)
 template <int S>
@@ -110,10 +115,10 @@ __device__ __forceinline__ void load_stage_gscales(const Ptrs& P, int kk, Stage<
     for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
 }
 
-template <int S, bool SL>
+template <int S, bool SL, bool PK>
 __device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
     Stage<S> st;
-    load_stage_mem<S>(P, kk, st);
+    load_stage_mem<S, PK>(P, kk, st);
     if constexpr (SL) load_stage_lds<S>(P, kk, st);
     else load_stage_gscales<S>(P, kk, st);
     return st;
@@ -172,7 +177,7 @@ __device__ __forceinline__ void stage_scales_issue(const GemmArgs& a, int e, int
     }
 }
 
-template <int MODE, int S, bool SL>
+template <int MODE, int S, bool SL, bool PK>
 __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
@@ -202,7 +207,9 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const size_t row = (size_t)e * wrows + wrow[j] + r;
-        P.w[j] = a.w + row * wstride + 16 * g;
+        // packed: the row's 16-row group, lane l's 16 bytes at 16 l of each block
+        if constexpr (PK) P.w[j] = a.w + (row - r) * wstride + 16 * lane;
+        else P.w[j] = a.w + row * wstride + 16 * g;
         P.s[j] = a.w_scale + row * sstride;
     }
     const int gshift = 8 * g;
@@ -238,8 +245,8 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         // the two stages issue kStageLoads loads each), then barrier
         stage_scales_issue<MODE>(a, e, K, row0, nrows);
         __builtin_amdgcn_sched_barrier(0);
-        load_stage_mem<S>(P, 0, s0);
-        load_stage_mem<S>(P, min(KS, klast), s1);
+        load_stage_mem<S, PK>(P, 0, s0);
+        load_stage_mem<S, PK>(P, min(KS, klast), s1);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kStageLoads));
         __builtin_amdgcn_s_barrier();
@@ -248,18 +255,18 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         load_stage_lds<S>(P, 0, s0);
         load_stage_lds<S>(P, min(KS, klast), s1);
     } else {
-        s0 = load_stage<S, SL>(P, 0);
-        s1 = load_stage<S, SL>(P, min(KS, klast));
+        s0 = load_stage<S, SL, PK>(P, 0);
+        s1 = load_stage<S, SL, PK>(P, min(KS, klast));
     }
     int kk = 0;
     for (; kk + 2 * KS <= K; kk += 2 * KS) {
         compute_stage<S, SL>(s0, acc, gshift);
         __builtin_amdgcn_sched_barrier(0);
-        s0 = load_stage<S, SL>(P, min(kk + 2 * KS, klast));
+        s0 = load_stage<S, SL, PK>(P, min(kk + 2 * KS, klast));
         __builtin_amdgcn_sched_barrier(0);
         compute_stage<S, SL>(s1, acc, gshift);
         __builtin_amdgcn_sched_barrier(0);
-        s1 = load_stage<S, SL>(P, min(kk + 3 * KS, klast));
+        s1 = load_stage<S, SL, PK>(P, min(kk + 3 * KS, klast));
         __builtin_amdgcn_sched_barrier(0);
     }
     if (kk < K) compute_stage<S, SL>(s0, acc, gshift);   // odd number of stages: the last one is in s0
@@ -310,7 +317,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     }
 }
 
-template <int MODE>
+template <int MODE, bool PK>
 static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     // grid.y: upper bound on m-tiles (sum over experts of ceil(n_e / 16));
     // workgroups past the real tile count exit at once.
@@ -318,16 +325,21 @@ static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     const int gx = (MODE == kGemm2) ? (a.H + 255) / 256 : a.I / 128;
     dim3 grid(gx, (unsigned)tiles), block(256);
     // stages of 256 K (two MFMA steps), two stages in flight per wave: about
-    // 16 KB of weights in flight per wave, over 100 KB per CU
+    // 16 KB of weights in flight per wave, over 100 KB per CU.
     // Scales are staged in LDS once per workgroup where they fit: per-stage
     // scale loads would cost as many memory requests as the weights.
     if (K % 512 == 0 && stream_lds_bytes(K) <= 65536)
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, true>), grid, block, stream_lds_bytes(K), stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, true, PK>), grid, block, stream_lds_bytes(K), stream, a);
     else if (K % 256 == 0)
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, false, PK>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1, false, PK>), grid, block, 0, stream, a);
     return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
+    return a.packed ? launch_mode<MODE, true>(a, K, stream) : launch_mode<MODE, false>(a, K, stream);
 }
 
 hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream) {

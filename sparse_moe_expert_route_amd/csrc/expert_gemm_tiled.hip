@@ -14,21 +14,30 @@
 //   result: acc[i] of lane l is D[8*(i/4) + 4g + (i%4)][r].
 // K is walked in stages of 256 = 4 MFMA steps; step s pairs logical 32-block
 // b with physical block 4b + s, so each lane's weight bytes for a stage are 64
-// contiguous bytes and its 4 weight scales one dword (op_sel = s).
+// contiguous bytes of its row and its 4 weight scales one dword (op_sel = s).
 //
 // Work decomposition: an item is (m-tile of 128 rows of one expert, n-block).
-// A workgroup of 4 waves computes 128 rows x (128 h-features = 256 W13 rows)
-// for the gate/up GEMM, or 128 rows x 256 output features for the down GEMM.
+// A workgroup of 8 waves (two per SIMD) computes 128 rows x (128 h-features =
+// 256 W13 rows) for the gate/up GEMM, or 128 rows x 256 output features for
+// the down GEMM; each wave owns one 32-row weight tile and all 128 rows.
 // The activation tile is staged through LDS by direct global->LDS loads
-// (global_load_lds_dwordx4: no staging registers), double-buffered, with the
-// 16-byte chunk c of row p stored at chunk slot c ^ (p mod 16) so that the 32
-// rows read by one MFMA operand fetch hit distinct banks; every wave streams
-// its own weight rows straight into registers.  The grid is persistent: workgroups on one XCD
-// (block id mod 8) take a contiguous 1/8 of the item list.  Items are grouped
-// by expert; an expert's m-tiles go in chunks of four, each chunk ordered
-// n-block major, m-tile minor: the m-tiles that read the same block of weight
-// rows run side by side on one L2 (weights come from HBM about once per
-// chunk), and the chunk's activations stay in L2 across its n-blocks.
+// (global_load_lds_dwordx4: no staging registers) in a three-buffer ring, with
+// the 16-byte chunk c of row p stored at chunk slot c ^ (p mod 16) so that the
+// 32 rows read by one MFMA operand fetch hit distinct banks; every wave
+// streams its own weight rows straight into registers.  The item's weight and
+// activation scales are copied to LDS once, at its start.
+//
+// Weight layouts: canonical (row-major codes) or the 16-row packed layout
+// written by moe_prepack_weights, in which one load instruction of a wave
+// covers whole 128-byte lines (a third of the address-unit time of the
+// row-strided canonical loads).
+//
+// The grid is persistent: workgroups on one XCD (block id mod 8) take a
+// contiguous 1/8 of the item list.  Items are grouped by expert; an expert's
+// m-tiles go in chunks of four, each chunk ordered n-block major, m-tile
+// minor: the m-tiles that read the same block of weight rows run side by
+// side on one L2 (weights come from HBM about once per chunk), and the
+// chunk's activations stay in L2 across its n-blocks.
 #include "moe_internal.h"
 
 #include <type_traits>
@@ -40,6 +49,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int kTileRows = 128;            // m-tile rows
 constexpr int kStageK = 256;              // K per LDS stage (bytes of an FP8 row)
 constexpr int kMChunk = 4;                // m-tiles of one expert scheduled together
+constexpr int kWaves = 8;                 // waves per workgroup, two per SIMD
+constexpr int kMaxK = 6144;               // largest K the LDS scale copies hold
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -47,10 +58,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 16, 0, 0);
 }
-// 2 bytes per lane, global -> LDS: the LDS slot of each lane is a dword
-// (lds_base + 4 * lane, upper half zero)
-__device__ __forceinline__ void dma2(const void* g, void* lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 2, 0, 0);
+// 4 bytes per lane, global -> LDS at lds_base + 4 * lane
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
 }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kStageK + ((chunk ^ (row & 15)) << 4); }
 
@@ -65,18 +75,19 @@ __device__ __forceinline__ v16f mfma32_w4a8(v8i a, v8i b, v16f c, int scale_a, i
 __shared__ __attribute__((aligned(16))) uint8_t tl_act0[kTileRows * kStageK];
 __shared__ __attribute__((aligned(16))) uint8_t tl_act1[kTileRows * kStageK];
 __shared__ __attribute__((aligned(16))) uint8_t tl_act2[kTileRows * kStageK];
-// activation scales: 2 bytes per row in dword slots; wave w's 32 rows at
-// slots 64w .. 64w+31 (its lanes 32..63 write a copy above them)
-__shared__ __attribute__((aligned(16))) uint32_t tl_scl0[2 * kTileRows];
-__shared__ __attribute__((aligned(16))) uint32_t tl_scl1[2 * kTileRows];
-__shared__ __attribute__((aligned(16))) uint32_t tl_scl2[2 * kTileRows];
+// the item's weight scales: 256 rows x K/32 bytes, the 16-byte chunks of row
+// R rotated by R (chunk c at slot (c + R) mod K/512), so that the 32 rows of
+// a wave read different banks
+__shared__ __attribute__((aligned(16))) uint8_t tl_wsc[256 * (kMaxK / 32)];
+// the item's activation scales: 128 rows x K/128 bytes, row-major
+__shared__ __attribute__((aligned(16))) uint8_t tl_xsc[kTileRows * (kMaxK / 128)];
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9
 // encoding, vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-// vector-memory operations one stage issues per wave: 8 activation pieces,
-// 1 activation-scale piece, 8 weight loads, 2 weight-scale loads
-constexpr int kStageLoads = 19;
+// vector-memory operations one stage issues per wave: 4 activation pieces and
+// 4 weight loads
+constexpr int kStageLoads = 8;
 
 // Workgroup barrier that waits on nothing: the callers first wait for their
 // own direct-to-LDS loads with an explicit vmcnt.  The empty asm statements
@@ -89,88 +100,96 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 struct WStage {
-    uint4 w[2][4];    // 2 weight tiles x 4 steps of 16 bytes
-    uint32_t ws[2];   // 4 scale bytes per tile
+    uint4 w[4];     // the wave's 32-row weight tile, 4 steps of 16 bytes
 };
 
 // Per-item state of the stage loop.
 struct TileCtx {
     const uint8_t* act;        // FP8 activations [N][K]
     const uint8_t* act_scale;  // [N][K/128]
-    const uint8_t* wp0;        // this lane's weight bytes, tile 0 (k = 0)
-    const uint8_t* wp1;        // tile 1
-    const uint8_t* sp0;        // this lane's weight scale bytes, tile 0
-    const uint8_t* sp1;        // tile 1
+    const uint8_t* wp;         // this lane's weight bytes at k = 0
+    const uint8_t* wscale;     // the expert's weight scales [rows][K/32]
+    int wstage, wstep;         // byte strides of wp per stage and per step
     int K, nstage, row0, nrows;
+    int nblk, I, H;
 };
 
-// The K loop of one item.  The three activation buffers come in as restrict
-// pointers: the compiler then tags every LDS access with the buffer it
-// touches, and its wait tracking for direct global->LDS loads (which would
-// otherwise make each LDS read wait for every such load in flight) lets a
-// buffer be read while the others are being filled.
-__device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4][2],
+// The K loop of one item.  The LDS buffers come in as restrict pointers: the
+// compiler then tags every LDS access with the buffer it touches, and its
+// wait tracking for direct global->LDS loads (which would otherwise make each
+// LDS read wait for every such load in flight) lets a buffer be read while
+// the others are being filled.
+template <int MODE, int PF_STEP>
+__device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4],
                                            uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
-                                           uint8_t* __restrict__ act2, uint32_t* __restrict__ scl0,
-                                           uint32_t* __restrict__ scl1, uint32_t* __restrict__ scl2) {
+                                           uint8_t* __restrict__ act2, uint8_t* __restrict__ wsc,
+                                           uint8_t* __restrict__ xsc) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, r = lane & 31;
     const int K = c.K, nstage = c.nstage, row0 = c.row0, nrows = c.nrows;
-    const uint8_t* wp0 = c.wp0; const uint8_t* wp1 = c.wp1;
-    const uint8_t* sp0 = c.sp0; const uint8_t* sp1 = c.sp1;
+    const uint8_t* wp = c.wp;
+    const int SB = K / 32, n16 = K / 512, XB = K / kFp8Block;
     auto abuf = [&](auto bc) -> uint8_t* {
         constexpr int B = decltype(bc)::value;
         if constexpr (B == 0) return act0; else if constexpr (B == 1) return act1; else return act2;
     };
-    auto sbuf = [&](auto bc) -> uint32_t* {
-        constexpr int B = decltype(bc)::value;
-        if constexpr (B == 0) return scl0; else if constexpr (B == 1) return scl1; else return scl2;
-    };
-    auto load_w = [&](WStage& ws, int st) {
-        const int kb = st * (kStageK / 2);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            ws.w[0][s] = *(const uint4*)(wp0 + kb + 16 * s);
-            ws.w[1][s] = *(const uint4*)(wp1 + kb + 16 * s);
+
+    // ---- the item's scales into LDS (waited for with the first stage) ----
+    // weight scales: 256 rows of n16 16-byte chunks, 64 chunks per load
+    for (int m = wave; m < 4 * n16; m += kWaves) {
+        const int i = 64 * m + lane, R = i / n16, slot = i - R * n16;
+        const int ch = (slot + n16 - R % n16) % n16;    // the chunk stored at this slot
+        int grow;                                       // the weight row of LDS row R
+        if constexpr (MODE == kGemm2) {
+            grow = min(c.nblk * 256 + R, c.H - 1);
+        } else {
+            const int w = R >> 5, rr = R & 31;
+            grow = (rr < 16 ? 0 : c.I - 16) + c.nblk * 128 + 16 * w + rr;
         }
-        ws.ws[0] = *(const uint32_t*)(sp0 + st * (kStageK / 32));
-        ws.ws[1] = *(const uint32_t*)(sp1 + st * (kStageK / 32));
+        dma16(c.wscale + (size_t)grow * SB + 16 * ch, wsc + 1024 * m);
+    }
+    // activation scales: 128 rows x XB bytes, 64 dwords per load
+    for (int m = wave; m < XB / 2; m += kWaves) {
+        const int i = 64 * m + lane, row = i / (XB / 4), col = i - row * (XB / 4);
+        dma4(c.act_scale + (size_t)(row0 + min(row, nrows - 1)) * XB + 4 * col, xsc + 256 * m);
+    }
+    const int R = 32 * wave + r;                        // this lane's LDS weight-scale row
+    const int rmod = R % n16;
+
+    // the wave's weight tile for stage st: 16 bytes per lane per step
+    auto load_w = [&](WStage& ws, int st) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ws.w[s] = *(const uint4*)(wp + st * c.wstage + s * c.wstep);
     };
 
-    // activation stage: 128 rows x 256 bytes.  Wave w moves rows 32w .. 32w+31,
+    // activation stage: 128 rows x 256 bytes.  Wave w moves rows 16w .. 16w+15,
     // four rows (64 lanes x 16 bytes) per instruction; lane i of an instruction
     // fills chunk slot i%16 of row 4p + i/16 with the global chunk that the
-    // swizzle maps there.  Every wave also moves the two scale bytes of its
-    // rows (twice: all 64 lanes), so that every wave issues kStageLoads loads.
+    // swizzle maps there.
     auto dma_act = [&](auto bufc, int st) {
-        const int k0 = st * kStageK;
         uint8_t* lds = abuf(bufc);
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const int row = 32 * wave + 4 * p + (lane >> 4);
+        for (int p = 0; p < 4; ++p) {
+            const int row = 16 * wave + 4 * p + (lane >> 4);
             const int chunk = (lane & 15) ^ (row & 15);
             const int rr = row0 + min(row, nrows - 1);
-            dma16(c.act + (size_t)rr * K + k0 + 16 * chunk, lds + (32 * wave + 4 * p) * kStageK);
-        }
-        {
-            const int rr = row0 + min(32 * wave + (lane & 31), nrows - 1);
-            dma2(c.act_scale + (size_t)rr * (K / kFp8Block) + k0 / kFp8Block, sbuf(bufc) + 64 * wave);
+            dma16(c.act + (size_t)rr * K + st * kStageK + 16 * chunk, lds + (16 * wave + 4 * p) * kStageK);
         }
     };
 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[j][t][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
 
     // Three-deep pipeline: stage st+2's activations (into LDS) and weights
     // (into a third register set) are issued while stage st is multiplied,
     // so each load has two stages of MFMA work to land.  Buffer and
     // register set of stage st are st mod 3; the stage loop is unrolled by
-    // three so that every set is a fixed set of registers.
+    // three so that every set is a fixed set of registers.  Two waves share
+    // each SIMD and issue their prefetch at different steps (PF_STEP): while
+    // one waits to issue its loads, the other's MFMAs run.
     WStage w0, w1, w2;
     auto stage = [&](auto setc, int st, const WStage& wc, WStage& wn) {
         constexpr int SET = decltype(setc)::value;
@@ -182,15 +201,23 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4][2],
         // so the body has no branch and the load count never changes.
         __builtin_amdgcn_s_waitcnt(vmcnt_only(kStageLoads));
         lds_barrier();
-        dma_act(std::integral_constant<int, NXT>{}, min(st + 2, nstage - 1));
-        load_w(wn, min(st + 2, nstage - 1));
-        __builtin_amdgcn_sched_barrier(0);
+        const int sp = min(st + 2, nstage - 1);
+        auto prefetch = [&]() {
+            dma_act(std::integral_constant<int, NXT>{}, sp);
+            load_w(wn, sp);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (PF_STEP == 0) prefetch();
         const uint8_t* lds = abuf(setc);
+        // scales of the stage: 4 weight-scale bytes of this lane's row
+        // (byte s for step s), one activation-scale byte per row tile
+        int slot = (st >> 1) + rmod;
+        if (slot >= n16) slot -= n16;
+        const int wsv = *(const int*)(wsc + R * SB + 16 * slot + 8 * (st & 1) + 4 * g);
         int bs[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bs[j] = (sbuf(setc)[64 * j + r] >> (8 * g)) & 0xFF;
-        // B operands one MFMA step ahead of their use
-        v8i B[2][4];
+        for (int j = 0; j < 4; ++j) bs[j] = xsc[(32 * j + r) * XB + 2 * st + g];
+        v8i B[4];
         auto read_b = [&](v8i (&Bd)[4], int s) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -201,39 +228,26 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4][2],
                 Bd[j][4] = hi4.x; Bd[j][5] = hi4.y; Bd[j][6] = hi4.z; Bd[j][7] = hi4.w;
             }
         };
-        read_b(B[0], 0);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if (s < 3) read_b(B[(s + 1) & 1], s + 1);
-            v8i A0, A1;
-            A0[0] = wc.w[0][s].x; A0[1] = wc.w[0][s].y; A0[2] = wc.w[0][s].z; A0[3] = wc.w[0][s].w;
-            A1[0] = wc.w[1][s].x; A1[1] = wc.w[1][s].y; A1[2] = wc.w[1][s].z; A1[3] = wc.w[1][s].w;
-            A0[4] = A0[5] = A0[6] = A0[7] = 0;
-            A1[4] = A1[5] = A1[6] = A1[7] = 0;
-            const v8i (&Bc)[4] = B[s & 1];
+            if (s == PF_STEP && s > 0) prefetch();
+            // B operands of one MFMA step (the other wave on the SIMD covers
+            // the LDS latency)
+            read_b(B, s);
+            v8i A;
+            A[0] = wc.w[s].x; A[1] = wc.w[s].y; A[2] = wc.w[s].z; A[3] = wc.w[s].w;
+            A[4] = A[5] = A[6] = A[7] = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 switch (s) {
-                    case 0:
-                        acc[j][0] = mfma32_w4a8<0>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
-                        acc[j][1] = mfma32_w4a8<0>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
-                        break;
-                    case 1:
-                        acc[j][0] = mfma32_w4a8<1>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
-                        acc[j][1] = mfma32_w4a8<1>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
-                        break;
-                    case 2:
-                        acc[j][0] = mfma32_w4a8<2>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
-                        acc[j][1] = mfma32_w4a8<2>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
-                        break;
-                    default:
-                        acc[j][0] = mfma32_w4a8<3>(A0, Bc[j], acc[j][0], (int)wc.ws[0], bs[j]);
-                        acc[j][1] = mfma32_w4a8<3>(A1, Bc[j], acc[j][1], (int)wc.ws[1], bs[j]);
-                        break;
+                    case 0: acc[j] = mfma32_w4a8<0>(A, B[j], acc[j], wsv, bs[j]); break;
+                    case 1: acc[j] = mfma32_w4a8<1>(A, B[j], acc[j], wsv, bs[j]); break;
+                    case 2: acc[j] = mfma32_w4a8<2>(A, B[j], acc[j], wsv, bs[j]); break;
+                    default: acc[j] = mfma32_w4a8<3>(A, B[j], acc[j], wsv, bs[j]); break;
                 }
             }
-            // keep each step's LDS reads next to the step before their use
-            // (hoisting them all would need every B operand of the stage live)
+            // keep each step's LDS reads next to their use (hoisting them
+            // all would need every B operand of the stage live)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -254,15 +268,14 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4][2],
     if (st < nstage) stage(I0{}, st, w0, w2);
     if (st + 1 < nstage) stage(I1{}, st + 1, w1, w0);
     // the tail prefetches have landed and every wave is done reading the
-    // ring before the next item refills it
+    // ring and the scale copies before the next item refills them
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     lds_barrier();
-
 }
 
-template <int MODE>
-__global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
-    __shared__ float red[4][kTileRows];
+template <int MODE, bool PACKED>
+__global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmArgs a) {
+    __shared__ float red[kWaves][kTileRows];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -295,75 +308,82 @@ __global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
         const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
         const int row0 = ti.y, nrows = ti.z;
 
-        // weight rows of this wave: two 32-row tiles
-        int wrow0, wrow1;
+        // weight rows of this wave: one 32-row tile.  Gate/up: rows 0..15 of
+        // the tile are gate features f0 .. f0+15 and rows 16..31 the up rows
+        // of the same features, so each lane ends up holding matching gate
+        // and up values (accumulator elements i and i + 8).
+        int wrow;
         bool wave_valid = true;
+        const int f0 = nblk * 128 + 16 * wave;
         if constexpr (MODE == kGemm2) {
-            wrow0 = nblk * 256 + wave * 64;
-            wrow1 = wrow0 + 32;
-            wave_valid = wrow0 < a.H;
-            if (!wave_valid) { wrow0 = 0; wrow1 = 32; }   // loads stay in bounds; results dropped
+            const int n0 = nblk * 256 + 32 * wave;
+            wave_valid = n0 < a.H;
+            wrow = (wave_valid ? n0 : 0) + r;   // loads stay in bounds; results dropped
         } else {
-            wrow0 = nblk * 128 + wave * 32;    // gate
-            wrow1 = a.I + wrow0;               // up
+            wrow = (r < 16) ? f0 + r : a.I + f0 + (r - 16);
         }
-        const size_t wstride = (size_t)K / 2, sstride = (size_t)K / 32;
-        const uint8_t* wp0 = a.w + ((size_t)e * wrows + wrow0 + r) * wstride + 64 * g;
-        const uint8_t* wp1 = a.w + ((size_t)e * wrows + wrow1 + r) * wstride + 64 * g;
-        const uint8_t* sp0 = a.w_scale + ((size_t)e * wrows + wrow0 + r) * sstride + 4 * g;
-        const uint8_t* sp1 = a.w_scale + ((size_t)e * wrows + wrow1 + r) * sstride + 4 * g;
-
         TileCtx c;
         c.act = a.act; c.act_scale = a.act_scale;
-        c.wp0 = wp0; c.wp1 = wp1; c.sp0 = sp0; c.sp1 = sp1;
+        const size_t erow = (size_t)e * wrows + wrow;
+        if constexpr (PACKED) {
+            // 16-row group of the row, K/128 blocks of 1 KB: lane (g, r) takes
+            // its 16 bytes of step s of stage st from block 2st + g, at
+            // 16 * (16s + r mod 16)
+            c.wp = a.w + (erow - (r & 15)) * ((size_t)K / 2) + 1024 * g + 16 * (r & 15);
+            c.wstage = 2048; c.wstep = 256;
+        } else {
+            c.wp = a.w + erow * ((size_t)K / 2) + 64 * g;
+            c.wstage = kStageK / 2; c.wstep = 16;
+        }
+        c.wscale = a.w_scale + (size_t)e * wrows * (K / 32);
         c.K = K; c.nstage = nstage; c.row0 = row0; c.nrows = nrows;
-        v16f acc[4][2];
-        tile_kloop(c, acc, tl_act0, tl_act1, tl_act2, tl_scl0, tl_scl1, tl_scl2);
+        c.nblk = nblk; c.I = a.I; c.H = a.H;
+        v16f acc[4];
+        // the two waves of a SIMD (w and w + 4) issue their prefetch half a
+        // stage apart, so that one multiplies while the other waits on the
+        // load queue
+        if (wave < 4) tile_kloop<MODE, 0>(c, acc, tl_act0, tl_act1, tl_act2, tl_wsc, tl_xsc);
+        else tile_kloop<MODE, 2>(c, acc, tl_act0, tl_act1, tl_act2, tl_wsc, tl_xsc);
 
-        // ---- epilogues: lane holds tokens 32j + r, features 8*(i/4) + 4g + (i%4) of each tile ----
+        // ---- epilogues: lane holds tokens 32j + r and tile rows 8*(i/4) + 4g + (i%4) ----
         if constexpr (MODE == kGemm2) {
             if (wave_valid) {
+                const int n0 = nblk * 256 + 32 * wave + 4 * g;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int rr = 32 * j + r;
                     if (rr >= nrows) continue;
-                    float* o = (float*)a.out + (size_t)(row0 + rr) * a.H;
+                    float* o = (float*)a.out + (size_t)(row0 + rr) * a.H + n0;
 #pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int n = (t == 0 ? wrow0 : wrow1) + 4 * g;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *(v4f*)(o + n + 8 * q) = v4f{acc[j][t][4 * q], acc[j][t][4 * q + 1],
-                                                         acc[j][t][4 * q + 2], acc[j][t][4 * q + 3]};
-                    }
+                    for (int q = 0; q < 4; ++q)
+                        *(v4f*)(o + 8 * q) = v4f{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
                 }
             }
         } else if constexpr (MODE == kGemm1Preact) {
+            // tile row 8q + 4g + i: q = 0, 1 gate features f0 + 8q + 4g + i, q = 2, 3 up
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rr = 32 * j + r;
                 if (rr >= nrows) continue;
                 float* o = (float*)a.out + (size_t)(row0 + rr) * (2 * a.I);
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int n = (t == 0 ? wrow0 : wrow1) + 4 * g;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *(v4f*)(o + n + 8 * q) = v4f{acc[j][t][4 * q], acc[j][t][4 * q + 1],
-                                                     acc[j][t][4 * q + 2], acc[j][t][4 * q + 3]};
+                for (int q = 0; q < 4; ++q) {
+                    const int n = (q < 2 ? f0 : a.I + f0) + 8 * (q & 1) + 4 * g;
+                    *(v4f*)(o + n) = v4f{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
                 }
             }
         } else {
-            // SwiGLU, then FP8 over the workgroup's 128 features per row
+            // SwiGLU on matching gate (element i) and up (element i + 8) values,
+            // then FP8 over the workgroup's 128 features of each row
             float amax[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float m = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float gv = acc[j][0][i];
-                    const float h = gv / (1.0f + __expf(-gv)) * acc[j][1][i];
-                    acc[j][0][i] = h;
+                for (int i = 0; i < 8; ++i) {
+                    const float gv = acc[j][i];
+                    const float h = gv / (1.0f + __expf(-gv)) * acc[j][i + 8];
+                    acc[j][i] = h;
                     m = fmaxf(m, fabsf(h));
                 }
                 m = fmaxf(m, __shfl_xor(m, 32, 64));
@@ -377,16 +397,18 @@ __global__ void __launch_bounds__(256, 1) expert_gemm_tiled_kernel(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rr = 32 * j + r;
-                const float m = fmaxf(fmaxf(red[0][rr], red[1][rr]), fmaxf(red[2][rr], red[3][rr]));
+                float m = red[0][rr];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][rr]);
                 const int ex = fp8_block_exponent(m);
                 if (rr < nrows) {
-                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + wrow0 + 4 * g;
+                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + f0 + 4 * g;
 #pragma unroll
-                    for (int qq = 0; qq < 4; ++qq)
-                        *(uint32_t*)(q + 8 * qq) = pack_fp8x4(__builtin_amdgcn_ldexpf(acc[j][0][4 * qq], -ex),
-                                                              __builtin_amdgcn_ldexpf(acc[j][0][4 * qq + 1], -ex),
-                                                              __builtin_amdgcn_ldexpf(acc[j][0][4 * qq + 2], -ex),
-                                                              __builtin_amdgcn_ldexpf(acc[j][0][4 * qq + 3], -ex));
+                    for (int qq = 0; qq < 2; ++qq)
+                        *(uint32_t*)(q + 8 * qq) = pack_fp8x4(__builtin_amdgcn_ldexpf(acc[j][4 * qq], -ex),
+                                                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -ex),
+                                                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -ex),
+                                                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -ex));
                     if (wave == 0 && g == 0)
                         a.out_scale[(size_t)(row0 + rr) * (a.I / kFp8Block) + nblk] = (uint8_t)(ex + 127);
                 }
@@ -408,15 +430,21 @@ static int persistent_grid() {
 }
 
 bool tiled_gemm_supported(int H, int I) {
-    return H % kStageK == 0 && I % kStageK == 0;
+    return H % 512 == 0 && I % 512 == 0 && H <= kMaxK && I <= kMaxK;
+}
+
+template <int MODE>
+static void launch_tiled_mode(const GemmArgs& a, hipStream_t stream) {
+    dim3 grid(persistent_grid()), block(64 * kWaves);
+    if (a.packed) hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, false>), grid, block, 0, stream, a);
 }
 
 hipError_t launch_expert_gemm_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream) {
-    dim3 grid(persistent_grid()), block(256);
     switch (mode) {
-        case kGemm1Swiglu: hipLaunchKernelGGL((expert_gemm_tiled_kernel<kGemm1Swiglu>), grid, block, 0, stream, a); break;
-        case kGemm1Preact: hipLaunchKernelGGL((expert_gemm_tiled_kernel<kGemm1Preact>), grid, block, 0, stream, a); break;
-        case kGemm2: hipLaunchKernelGGL((expert_gemm_tiled_kernel<kGemm2>), grid, block, 0, stream, a); break;
+        case kGemm1Swiglu: launch_tiled_mode<kGemm1Swiglu>(a, stream); break;
+        case kGemm1Preact: launch_tiled_mode<kGemm1Preact>(a, stream); break;
+        case kGemm2: launch_tiled_mode<kGemm2>(a, stream); break;
     }
     return hipGetLastError();
 }

@@ -76,6 +76,11 @@ hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, co
 hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq,
                                uint8_t* xs, int64_t N, int H, int64_t T, hipStream_t stream);
 
+// Byte permutation of a matrix of `rows` rows x K e2m1 columns (K/2 bytes per
+// row, rows a multiple of 16, K a multiple of 128) into the packed weight
+// layout of moe.h (MOE_WEIGHTS_PACKED).
+hipError_t launch_prepack(const uint8_t* src, uint8_t* dst, int64_t rows, int K, hipStream_t stream);
+
 // tile_info[t] = {expert, first row, rows} of m-tile t for t < max_tiles
 // (expert -1 past the last tile); max_tiles = ceil(N / rows_per_tile) + E.
 hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, int E, int rows_per_tile,
@@ -99,12 +104,13 @@ struct GemmArgs {
     uint8_t* out_scale;        // swiglu: hs [N][I/128]
     int64_t N;
     int H, I, E;
+    int packed;                // weight codes in the 16-row packed layout (moe_prepack_weights)
 };
 constexpr int kRowsPerTile = 16;   // rows per m-tile of the streaming expert GEMM
 hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream);
 
 // LDS-tiled variant for many rows per expert: m-tiles of 128 rows, needs
-// H and I multiples of 256.
+// H and I multiples of 512, at most 6144.
 constexpr int kRowsPerTileTiled = 128;
 bool tiled_gemm_supported(int H, int I);
 hipError_t launch_expert_gemm_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream);

@@ -39,9 +39,25 @@ def host(t):
     return t.cpu().numpy()
 
 
-def weights(layer):
+def weights(layer, packed=False):
+    """Device expert weights of a layer; packed=True reorders the codes with moe_prepack_weights."""
     import sparse_moe_expert_route_amd as moe
-    return moe.ExpertWeights(dev(layer["w13"]), dev(layer["w13_s"]), dev(layer["w2"]), dev(layer["w2_s"]))
+    W = moe.ExpertWeights(dev(layer["w13"]), dev(layer["w13_s"]), dev(layer["w2"]), dev(layer["w2_s"]))
+    if not packed:
+        return W
+    T, H = layer["x"].shape
+    E, k = layer["w13"].shape[0], layer["top_k"]
+    p = moe.Problem.make(T, H, layer["w2"].shape[2] * 2, E, k)
+    return moe.prepack_weights(p, W)
+
+
+def pack_codes_reference(codes):
+    """The packed layout of moe.h written out in numpy: codes [R, K/2] uint8 (R % 16 == 0,
+    K % 128 == 0) -> [R * K/2] uint8 with row 16q + r, bytes [64c + 16p, +16) of step c at
+    block (q, c), offset (16p + r) * 16."""
+    R, KB = codes.shape
+    u = codes.reshape(R // 16, 16, KB // 64, 4, 16)        # q, r, c, p, byte
+    return np.ascontiguousarray(u.transpose(0, 2, 3, 1, 4)).reshape(-1)
 
 
 def problem(layer):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     for st, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"), (4, b"HIP launch failure")]:
         assert lib.moe_status_string(st) == text
     assert lib.moe_status_string(99) == b"unknown status"
@@ -68,8 +68,8 @@ def test_workspace_size_covers_intermediates(lib):
 FAKE = 1 << 20   # an aligned non-null address; never dereferenced (every call below fails validation or is a no-op)
 
 
-def _w(ptr=FAKE):
-    return moe._Weights(ptr, ptr, ptr, ptr)
+def _w(ptr=FAKE, layout=0):
+    return moe._Weights(ptr, ptr, ptr, ptr, layout)
 
 
 def test_invalid_arguments_rejected_before_launch(lib):
@@ -98,6 +98,18 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert lib.moe_forward(ctypes.byref(pb), vp(FAKE), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 0, vp(FAKE), big,
                            None) == 1
     assert lib.moe_forward(None, vp(FAKE), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 0, vp(FAKE), big, None) == 1
+    # unknown weight layout
+    wl = _w(layout=7)
+    assert lib.moe_forward(ctypes.byref(p), vp(FAKE), vp(FAKE), None, ctypes.byref(wl), vp(FAKE), 0, vp(FAKE), big,
+                           None) == 1
+    # prepack: source must be canonical; outputs aligned and not overlapping the inputs or each other
+    wp = _w(layout=1)
+    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(wp), vp(2 * FAKE), vp(3 * FAKE), None) == 1
+    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(2 * FAKE + 8), vp(3 * FAKE), None) == 1
+    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(FAKE + 16), vp(3 * FAKE), None) == 1
+    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(2 * FAKE), vp(2 * FAKE + 256), None) == 1
+    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w0), vp(2 * FAKE), vp(3 * FAKE), None) == 1
+    assert lib.moe_prepack_weights(ctypes.byref(pb), ctypes.byref(w), vp(2 * FAKE), vp(3 * FAKE), None) == 1
     # unsupported scoring function
     ps = _P(sf=1)
     assert lib.moe_route(ctypes.byref(ps), None, None, None, vp(FAKE), vp(FAKE), vp(FAKE), None) == 2

@@ -55,18 +55,23 @@ def _forward(moe, lay, p, W, out_dtype=0, ws=None):
     return host(y)
 
 
-SMALL = [("tiny", {}), ("tiny", dict(bias="zipf", E=32, k=4, T=100)), ("tiny", dict(T=1)),
-         ("tiny", dict(E=4, k=4, T=33)), ("tiny", dict(k=1, T=70)), ("tiny", dict(T=129, H=512, I=256, E=24, k=8)),
-         ("tiny", dict(T=40, H=1024, I=640, E=12, k=3)),
-         ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf")), ("tiny", dict(T=300, H=256, I=256, E=8, k=8))]
+SMALL = [("tiny", {}, False), ("tiny", dict(bias="zipf", E=32, k=4, T=100), False), ("tiny", dict(T=1), False),
+         ("tiny", dict(E=4, k=4, T=33), False), ("tiny", dict(k=1, T=70), False),
+         ("tiny", dict(T=129, H=512, I=256, E=24, k=8), False), ("tiny", dict(T=40, H=1024, I=640, E=12, k=3), False),
+         ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), False),
+         ("tiny", dict(T=300, H=256, I=256, E=8, k=8), False),
+         # packed weights: streaming and tiled kernels
+         ("tiny", dict(T=129, H=512, I=256, E=24, k=8), True), ("tiny", dict(T=40, H=1024, I=640, E=12, k=3), True),
+         ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), True),
+         ("tiny", dict(T=400, H=1024, I=1536, E=16, k=8), True)]
 
 
-@pytest.mark.parametrize("cfg,over", SMALL)
-def test_forward_small_parity(moe, cfg, over):
+@pytest.mark.parametrize("cfg,over,packed", SMALL)
+def test_forward_small_parity(moe, cfg, over, packed):
     lay = S.make_layer(cfg, seed=0, **over)
     p = problem(lay)
-    log("forward %s %s" % (cfg, over))
-    W = weights(lay)
+    log("forward %s %s packed=%s" % (cfg, over, packed))
+    W = weights(lay, packed)
     y = _forward(moe, lay, p, W)
     ref = oracle_with_allowance(lay)
     L_ref = ref["logits"]
@@ -84,13 +89,14 @@ def test_forward_small_parity(moe, cfg, over):
     assert np.array_equal(_forward(moe, lay, p, W), y)
 
 
-def test_staged_entry_points_equal_forward(moe):
+@pytest.mark.parametrize("packed", [False, True])
+def test_staged_entry_points_equal_forward(moe, packed):
     lay = S.make_layer("tiny", seed=4, T=200, E=16, k=4, bias="zipf")
     p = problem(lay)
     T, H = lay["x"].shape
     E, k, inter = p.num_experts, p.top_k, p.intermediate
     N = T * k
-    W = weights(lay)
+    W = weights(lay, packed)
     y_fused = _forward(moe, lay, p, W)
     ws = moe.alloc_workspace(p)
     x = dev(lay["x"])
@@ -119,19 +125,22 @@ def test_staged_entry_points_equal_forward(moe):
     checks.check_permutation(host(ids), host(off), host(st), host(ros))
 
 
-FULL = ["tiny", "flash_decode", "pro_decode", "flash_prefill", "pro_skewed_prefill"]
+# the benchmarked path (packed weights) on every workload, and canonical
+# weights on one decode and one prefill workload
+FULL = [("tiny", True), ("flash_decode", True), ("pro_decode", True), ("flash_prefill", True),
+        ("pro_skewed_prefill", True), ("flash_decode", False), ("flash_prefill", False)]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg", FULL)
-def test_forward_full_size_sampled(moe, cfg):
-    log("full-size %s: generating layer" % cfg)
+@pytest.mark.parametrize("cfg,packed", FULL)
+def test_forward_full_size_sampled(moe, cfg, packed):
+    log("full-size %s packed=%s: generating layer" % (cfg, packed))
     lay = S.make_layer(cfg, seed=0)
     p = problem(lay)
     T, H = lay["x"].shape
     E, k = p.num_experts, p.top_k
     log("  uploading")
-    W = weights(lay)
+    W = weights(lay, packed)
     ws = moe.alloc_workspace(p)
     log("  forward")
     y = _forward(moe, lay, p, W, ws=ws)

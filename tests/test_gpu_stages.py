@@ -17,7 +17,7 @@ from oracle import checks
 from oracle import formats as F
 from oracle import layer as OL
 from moe_testutil import (dev, host, log, weights, logit_tol, unambiguous_tokens, key_margin, WEIGHT_ATOL, ACC_REL,
-                          h_rounding_allowance)
+                          h_rounding_allowance, pack_codes_reference)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,15 +151,37 @@ def _offsets_for(T, E, k, seed, skew=None):
     return OL.permutation(ids, E)["offsets"]
 
 
-# the first five shapes run the weight-streaming kernel (few rows per expert),
-# the last three the LDS-tiled kernel (>= 32 rows per expert on average)
+# ---------------------------------------------------------------------------
+# packed weight layout: a byte permutation, checked against its definition
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,I,E", [(256, 128, 3), (4096, 2048, 2), (384, 640, 5), (6144, 512, 1)])
+def test_prepack_bitexact(moe, H, I, E):
+    log("prepack H=%d I=%d E=%d" % (H, I, E))
+    rng = np.random.default_rng(H + I + E)
+    w13 = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
+    w2 = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
+    s13 = np.zeros((E, 2 * I, H // 32), np.uint8)
+    s2 = np.zeros((E, H, I // 32), np.uint8)
+    p = moe.Problem.make(1, H, I, E, 1)
+    Wp = moe.prepack_weights(p, moe.ExpertWeights(dev(w13), dev(s13), dev(w2), dev(s2)))
+    torch.cuda.synchronize()
+    assert Wp.layout == moe.WEIGHTS_PACKED
+    assert np.array_equal(host(Wp.w13).reshape(-1), pack_codes_reference(w13.reshape(E * 2 * I, H // 2)))
+    assert np.array_equal(host(Wp.w2).reshape(-1), pack_codes_reference(w2.reshape(E * H, I // 2)))
+
+
+# Shapes with few rows per expert run the weight-streaming kernel; those with
+# >= 32 rows per expert on average and H, I multiples of 512 (at most 6144)
+# the LDS-tiled kernel.  Each runs with canonical and with packed weights.
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T,H,I,E,k,skew", [(64, 256, 128, 8, 2, None), (40, 512, 256, 16, 4, 3.0),
                                             (9, 4096, 2048, 8, 8, None), (150, 1024, 384, 12, 3, 2.0),
                                             (3, 6144, 256, 4, 2, None), (300, 512, 512, 8, 4, 2.0),
                                             (200, 1024, 256, 16, 8, None), (700, 256, 768, 8, 2, 6.0),
-                                            (5, 8192, 256, 4, 2, None)])
-def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
-    log("gemm1 lossless T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
+                                            (5, 8192, 256, 4, 2, None), (200, 1024, 512, 16, 8, None),
+                                            (700, 512, 1536, 8, 2, 6.0), (150, 6144, 512, 8, 4, 1.5)])
+def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew, packed):
+    log("gemm1 lossless T=%d H=%d I=%d E=%d k=%d packed=%s" % (T, H, I, E, k, packed))
     N = T * k
     off = _offsets_for(T, E, k, seed=H + I, skew=skew)
     a, a_s, w13, w13_s = S.lossless_gemm_inputs(N, H, 2 * I, seed=1, batch=E)
@@ -167,6 +189,8 @@ def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
     p = moe.Problem.make(T, H, I, E, k)
     ws = moe.alloc_workspace(p)
     W = moe.ExpertWeights(dev(w13), dev(w13_s), dev(w2), dev(w2_s))
+    if packed:
+        W = moe.prepack_weights(p, W)
     gu = torch.full((N, 2 * I), float("nan"), dtype=torch.float32, device="cuda")
     moe.grouped_gemm1_preact(p, dev(a), dev(a_s), dev(off), W, gu, ws)
     torch.cuda.synchronize()
@@ -179,11 +203,12 @@ def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew):
     assert np.array_equal(host(gu).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 8, 2), (40, 512, 256, 16, 4), (9, 4096, 2048, 8, 8),
                                        (33, 384, 640, 5, 2), (300, 512, 512, 8, 4), (200, 1280, 256, 16, 8),
-                                       (50, 384, 512, 6, 2)])
-def test_gemm2_lossless_bitexact(moe, T, H, I, E, k):
-    log("gemm2 lossless T=%d H=%d I=%d E=%d k=%d" % (T, H, I, E, k))
+                                       (50, 384, 512, 6, 2), (200, 1536, 1024, 16, 8), (150, 6144, 512, 8, 4)])
+def test_gemm2_lossless_bitexact(moe, T, H, I, E, k, packed):
+    log("gemm2 lossless T=%d H=%d I=%d E=%d k=%d packed=%s" % (T, H, I, E, k, packed))
     N = T * k
     off = _offsets_for(T, E, k, seed=7 + H)
     hq, hs, w2, w2_s = S.lossless_gemm_inputs(N, I, H, seed=3, batch=E)
@@ -191,6 +216,8 @@ def test_gemm2_lossless_bitexact(moe, T, H, I, E, k):
     p = moe.Problem.make(T, H, I, E, k)
     ws = moe.alloc_workspace(p)
     W = moe.ExpertWeights(dev(w13), dev(w13_s), dev(w2), dev(w2_s))
+    if packed:
+        W = moe.prepack_weights(p, W)
     y = torch.full((N, H), float("nan"), dtype=torch.float32, device="cuda")
     moe.grouped_gemm2(p, dev(hq), dev(hs), dev(off), W, y, ws)
     torch.cuda.synchronize()
@@ -206,15 +233,16 @@ def test_gemm2_lossless_bitexact(moe, T, H, I, E, k):
 # ---------------------------------------------------------------------------
 # SwiGLU + FP8 requantisation epilogue on random operands
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("cfg,over", [("tiny", {}), ("tiny", dict(T=90, H=512, I=384, E=16, k=4)),
                                       ("flash_decode", dict(E=16, T=24)), ("tiny", dict(T=400, H=512, I=512, E=8, k=4)),
-                                      ("flash_decode", dict(E=8, T=160))])
-def test_gemm1_swiglu_parity(moe, cfg, over):
+                                      ("flash_decode", dict(E=8, T=160)), ("tiny", dict(T=300, H=1024, I=1024, E=8, k=4))])
+def test_gemm1_swiglu_parity(moe, cfg, over, packed):
     lay = S.make_layer(cfg, seed=5, **over)
     T, H = lay["x"].shape
     E, k = lay["w13"].shape[0], lay["top_k"]
     inter = lay["w2"].shape[2] * 2
-    log("gemm1 swiglu %s %s" % (cfg, over))
+    log("gemm1 swiglu %s %s packed=%s" % (cfg, over, packed))
     N = T * k
     ids = S.random_ids(T, E, k, seed=11)
     perm = OL.permutation(ids, E)
@@ -224,7 +252,7 @@ def test_gemm1_swiglu_parity(moe, cfg, over):
     ws = moe.alloc_workspace(p)
     hq = torch.empty(N, inter, dtype=torch.uint8, device="cuda")
     hs = torch.empty(N, inter // 128, dtype=torch.uint8, device="cuda")
-    moe.grouped_gemm1_swiglu(p, dev(xq), dev(xs), dev(perm["offsets"]), weights(lay), hq, hs, ws)
+    moe.grouped_gemm1_swiglu(p, dev(xq), dev(xs), dev(perm["offsets"]), weights(lay, packed), hq, hs, ws)
     torch.cuda.synchronize()
     A = F.dequantize_fp8_blocks(xq, xs)
     off = perm["offsets"]
