@@ -5,6 +5,8 @@
 // on the teardown page.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 // ---------------------------------------------------------------------------
@@ -100,6 +102,136 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
     }
 }
 
+// ---------------------------------------------------------------------------
+// Router logits for many tokens (prefill): an LDS-tiled bf16 GEMM on
+// v_mfma_f32_32x32x16_bf16.  A workgroup of 4 waves computes 64 tokens x 128
+// experts (small enough for two workgroups per CU and, on the prefill
+// shapes, at least one workgroup per CU); wave (wm, wn) owns 32 tokens x 64
+// experts (1 x 2 MFMA tiles).  K is walked in stages of 64 (128 bytes of a
+// bf16 row); each stage's 64 x rows and 128 W_r rows (24 KB) are copied by
+// direct global->LDS loads into a three-buffer ring, two stages ahead of
+// their use, with the 16-byte chunk c
+// of row p stored at slot c ^ (p mod 8) so that the 32 rows of one operand
+// fetch hit distinct banks.  Both operands use the same lane -> k mapping
+// (8 consecutive k per lane), which is all a dot product needs.  Rows past T
+// or E are clamped for loading and not stored.  H % 64 == 0.
+// ---------------------------------------------------------------------------
+typedef float v16f_r __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_r;
+
+constexpr int kRtTok = 64;           // tokens per workgroup
+constexpr int kRtExp = 128;          // experts per workgroup
+constexpr int kRtStageK = 64;        // bf16 elements of K per stage
+constexpr int kRtRowBytes = 2 * kRtStageK;
+constexpr int kRtBuf = (kRtTok + kRtExp) * kRtRowBytes;   // x rows, then W_r rows
+constexpr int kRtLoads = (kRtTok + kRtExp) / 32;          // direct loads per wave per stage (8 rows each)
+
+__shared__ __attribute__((aligned(16))) uint8_t rt_buf0[kRtBuf];
+__shared__ __attribute__((aligned(16))) uint8_t rt_buf1[kRtBuf];
+__shared__ __attribute__((aligned(16))) uint8_t rt_buf2[kRtBuf];
+
+__device__ __forceinline__ int rt_swz(int row, int chunk) { return row * kRtRowBytes + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ constexpr int rt_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// The K loop; the three LDS buffers come in as restrict pointers so that the
+// compiler's wait tracking for direct-to-LDS loads tells them apart.
+__device__ __forceinline__ void router_tiled_kloop(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                   int T, int H, int E, int t0, int e0, v16f_r (&acc)[2],
+                                                   uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
+                                                   uint8_t* __restrict__ b2) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, r = lane & 31;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int nstage = H / kRtStageK;
+    auto buf = [&](auto bc) -> uint8_t* {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (B == 0) return b0; else if constexpr (B == 1) return b1; else return b2;
+    };
+    // stage st: 192 rows (64 x rows, then 128 W_r rows) x 128 bytes; each
+    // load moves 8 rows (8 lanes of 16 bytes per row); wave w moves rows
+    // 48w .. 48w+47
+    auto load_stage = [&](auto bc, int st) {
+        uint8_t* lds = buf(bc);
+#pragma unroll
+        for (int p = 0; p < kRtLoads; ++p) {
+            const int row = 8 * kRtLoads * wave + 8 * p + (lane >> 3);    // 0..191
+            const int chunk = (lane & 7) ^ (row & 7);
+            const uint16_t* src = (row < kRtTok) ? x + (size_t)min(t0 + row, T - 1) * H
+                                                 : wr + (size_t)min(e0 + row - kRtTok, E - 1) * H;
+            __builtin_amdgcn_global_load_lds(src + st * kRtStageK + 8 * chunk,
+                                             (lds_void_r*)(lds + (8 * kRtLoads * wave + 8 * p) * kRtRowBytes), 16, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[j][q] = 0.0f;
+
+    auto stage = [&](auto setc, int st) {
+        constexpr int SET = decltype(setc)::value;
+        // stage st landed in every wave; the buffer of stage st-1 is free
+        __builtin_amdgcn_s_waitcnt(rt_vmcnt(kRtLoads));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load_stage(std::integral_constant<int, (SET + 2) % 3>{}, min(st + 2, nstage - 1));
+        const uint8_t* lds = buf(setc);
+#pragma unroll
+        for (int s = 0; s < kRtStageK / 16; ++s) {
+            const v8bf xa = *(const v8bf*)(lds + rt_swz(32 * wm + r, 2 * s + g));
+            v8bf wa[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) wa[j] = *(const v8bf*)(lds + rt_swz(kRtTok + 64 * wn + 32 * j + r, 2 * s + g));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa[j], xa, acc[j], 0, 0, 0);
+        }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    load_stage(I0{}, 0);
+    load_stage(I1{}, min(1, nstage - 1));
+    int st = 0;
+    for (; st + 3 <= nstage; st += 3) {
+        stage(I0{}, st);
+        stage(I1{}, st + 1);
+        stage(I2{}, st + 2);
+    }
+    if (st < nstage) stage(I0{}, st);
+    if (st + 1 < nstage) stage(I1{}, st + 1);
+    __builtin_amdgcn_s_waitcnt(rt_vmcnt(0));
+}
+
+__global__ void __launch_bounds__(256) router_logits_tiled_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ wr,
+                                                                   float* __restrict__ logits, int T, int H, int E) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, r = lane & 31;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int e0 = blockIdx.x * kRtExp, t0 = blockIdx.y * kRtTok;
+    v16f_r acc[2];
+    router_tiled_kloop(x, wr, T, H, E, t0, e0, acc, rt_buf0, rt_buf1, rt_buf2);
+    // acc[j]: token t0 + 32wm + r, experts e0 + 64wn + 32j + 8q + 4g + (0..3)
+    const int t = t0 + 32 * wm + r;
+    if (t >= T) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = e0 + 64 * wn + 32 * j + 8 * q + 4 * g;
+            float* o = logits + (size_t)t * E + e;
+            const v4f v = {acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+            if (e + 3 < E && (E & 3) == 0) {
+                *(v4f*)o = v;
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (e + u < E) o[u] = v[u];
+            }
+        }
+    }
+}
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, float* logits,
                                 int64_t T, int H, int E, hipStream_t stream) {
     if (T <= 256) {
@@ -108,10 +240,10 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, flo
         hipLaunchKernelGGL((router_logits_kernel<1, 4>), grid, dim3(256), 0, stream, x, w_router, logits,
                            (int)T, H, E);
     } else {
-        // prefill shapes: 64 tokens x 64 experts per workgroup
-        dim3 grid((E + 63) / 64, (unsigned)((T + 63) / 64));
-        hipLaunchKernelGGL((router_logits_kernel<4, 1>), grid, dim3(256), 0, stream, x, w_router, logits,
-                           (int)T, H, E);
+        // prefill shapes: LDS-tiled, 64 tokens x 128 experts per workgroup,
+        // expert blocks fastest so the workgroups sharing a block of x run together
+        dim3 grid((E + kRtExp - 1) / kRtExp, (unsigned)((T + kRtTok - 1) / kRtTok));
+        hipLaunchKernelGGL(router_logits_tiled_kernel, grid, dim3(256), 0, stream, x, w_router, logits, (int)T, H, E);
     }
     return hipGetLastError();
 }
