@@ -108,16 +108,31 @@ moe_status run_route(const moe_problem& p, const void* x, const void* wr, const 
     return MOE_OK;
 }
 
+bool use_tiled(const moe_problem& p);
+
+// Permutation and FP8 gather.  Up to kPermBlock slots (decode) one workgroup
+// does the whole permutation and also writes the GEMMs' tile plan into the
+// workspace; *planned tells the caller that it may skip the plan.
 moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, int32_t* offsets,
                        int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, uint8_t* xs, void* ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, bool* planned = nullptr) {
     const Layout L = layout_of(p);
     const int64_t N = p.num_tokens * p.top_k;
-    int32_t* bc = at<int32_t>(ws, L.block_counts);
-    int32_t* bb = at<int32_t>(ws, L.block_base);
-    MOE_LAUNCH(launch_perm_count(ids, bc, N, p.num_experts, stream));
-    MOE_LAUNCH(launch_perm_scan(bc, bb, offsets, N, p.num_experts, stream));
-    MOE_LAUNCH(launch_perm_scatter(ids, bb, offsets, sorted_token, row_of_slot, N, p.num_experts, p.top_k, stream));
+    if (N <= kPermBlock) {
+        const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
+        MOE_LAUNCH(launch_perm_small(ids, offsets, sorted_token, row_of_slot, at<int32_t>(ws, L.tile_start),
+                                     at<int4>(ws, L.tile_info), N, p.num_experts, p.top_k, rpt,
+                                     max_tiles(N, p.num_experts, rpt), stream));
+        if (planned) *planned = true;
+    } else {
+        int32_t* bc = at<int32_t>(ws, L.block_counts);
+        int32_t* bb = at<int32_t>(ws, L.block_base);
+        MOE_LAUNCH(launch_perm_count(ids, bc, N, p.num_experts, stream));
+        MOE_LAUNCH(launch_perm_scan(bc, bb, offsets, N, p.num_experts, stream));
+        MOE_LAUNCH(launch_perm_scatter(ids, bb, offsets, sorted_token, row_of_slot, N, p.num_experts, p.top_k,
+                                       stream));
+        if (planned) *planned = false;
+    }
     MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens, stream));
     return MOE_OK;
 }
@@ -322,8 +337,9 @@ moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_r
     uint8_t* hs = at<uint8_t>(ws, L.hs);
     float* y_perm = at<float>(ws, L.y_perm);
     MOE_CHECK(run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, ids, w, stream));
-    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream));
-    MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq, xs, offsets, *weights, hq, hs, ws, true, stream));
+    bool planned = false;
+    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream, &planned));
+    MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq, xs, offsets, *weights, hq, hs, ws, !planned, stream));
     MOE_CHECK(run_gemm2(*p, hq, hs, offsets, *weights, y_perm, ws, false, stream));
     MOE_LAUNCH(launch_combine(y_perm, ros, w, y, out_dtype == MOE_OUT_BF16, p->num_tokens, p->hidden, p->top_k,
                               stream));

@@ -18,7 +18,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
         rows[j] = j < k ? row_of_slot[(size_t)t * k + j] : -1;
         ws[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
     }
-    for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+    // workgroup (t, b) covers channels [1024 b, 1024 b + 1024): a decode step
+    // with few tokens still spreads over the whole chip
+    for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < H; c += gridDim.y * 256 * 4) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -43,7 +45,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y, int out_bf16,
                           int64_t T, int H, int k, hipStream_t stream) {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T), dim3(256), 0, stream, y_perm, row_of_slot, w, y, out_bf16,
+    const unsigned cb = (unsigned)((H + 1023) / 1024);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T, cb), dim3(256), 0, stream, y_perm, row_of_slot, w, y, out_bf16,
                        (int)T, H, k);
     return hipGetLastError();
 }

@@ -73,6 +73,10 @@ hipError_t launch_perm_scan(const int32_t* block_counts, int32_t* block_base, in
 hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, const int32_t* offsets,
                                int32_t* sorted_token, int32_t* row_of_slot, int64_t N, int E, int k,
                                hipStream_t stream);
+// count + scan + scatter + tile plan in one workgroup, for N <= kPermBlock
+hipError_t launch_perm_small(const int32_t* ids, int32_t* offsets, int32_t* sorted_token, int32_t* row_of_slot,
+                             int32_t* tile_start, int4* tile_info, int64_t N, int E, int k, int rows_per_tile,
+                             int max_tiles, hipStream_t stream);
 hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq,
                                uint8_t* xs, int64_t N, int H, int64_t T, hipStream_t stream);
 

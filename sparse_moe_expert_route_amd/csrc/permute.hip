@@ -99,6 +99,105 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
     sorted_token[row] = s / k;
 }
 
+// ---------------------------------------------------------------------------
+// All of the permutation for at most kPermBlock slots (decode), plus the
+// grouped GEMMs' tile plan, in one workgroup: expert histogram, the two
+// exclusive scans (rows and m-tiles), the stable in-block rank of every slot
+// (the ballot match of perm_scatter_kernel) and the per-tile descriptors.
+// One launch instead of four.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* __restrict__ ids,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ sorted_token,
+                                                                int32_t* __restrict__ row_of_slot,
+                                                                int32_t* __restrict__ tile_start,
+                                                                int4* __restrict__ tile_info,
+                                                                int N, int E, int k, int rpt, int max_tiles) {
+    __shared__ int cnt[512];
+    __shared__ int2 scan[512];          // (rows, tiles) inclusive prefix
+    __shared__ int off[513], tst[513];
+    __shared__ int wcnt[kPermBlock / 64][512];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < 512; i += kPermBlock) cnt[i] = 0;
+    for (int i = tid; i < (kPermBlock / 64) * 512; i += kPermBlock) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int id = tid < N ? ids[tid] : -1;
+    const bool valid = (unsigned)id < (unsigned)E;
+    const int e = valid ? id : 1023;    // 1023 never equals a real id (E <= 512)
+    if (valid) atomicAdd(&cnt[e], 1);   // counts only; no position depends on the order
+    __syncthreads();
+    // inclusive scan of (rows, tiles) over 512 experts: Hillis-Steele on threads 0..511
+    int n = 0, nt = 0;
+    if (tid < 512) {
+        n = tid < E ? cnt[tid] : 0;
+        nt = (n + rpt - 1) / rpt;
+        scan[tid] = int2{n, nt};
+    }
+    __syncthreads();
+    for (int d = 1; d < 512; d <<= 1) {
+        int2 v = int2{0, 0};
+        if (tid < 512 && tid >= d) v = scan[tid - d];
+        __syncthreads();
+        if (tid < 512) { scan[tid].x += v.x; scan[tid].y += v.y; }
+        __syncthreads();
+    }
+    if (tid < E) {
+        off[tid] = scan[tid].x - n;
+        tst[tid] = scan[tid].y - nt;
+        offsets[tid] = scan[tid].x - n;
+        tile_start[tid] = scan[tid].y - nt;
+    }
+    if (tid == E - 1) {
+        off[E] = scan[tid].x; tst[E] = scan[tid].y;
+        offsets[E] = scan[tid].x; tile_start[E] = scan[tid].y;
+    }
+    // stable rank of each slot among the slots of its expert
+    unsigned long long m = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+        const unsigned long long b = __ballot((e >> bit) & 1);
+        m &= ((e >> bit) & 1) ? b : ~b;
+    }
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(m & lt);
+    if (valid && rank == 0) wcnt[wave][e] = __popcll(m);
+    __syncthreads();
+    if (tid < N) {
+        if (valid) {
+            int pre = 0;
+            for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+            const int row = off[e] + pre + rank;
+            row_of_slot[tid] = row;
+            sorted_token[row] = tid / k;
+        } else {
+            row_of_slot[tid] = -1;   // an out-of-range id gets no row
+        }
+    }
+    // per-tile descriptors {expert, first row, rows}; expert -1 past the last tile
+    const int ntiles = tst[E];
+    for (int t = tid; t < max_tiles; t += kPermBlock) {
+        int4 info = {-1, 0, 0, 0};
+        if (t < ntiles) {
+            int lo = 0, hi = E - 1;   // largest expert whose first tile is <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (tst[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int row0 = off[lo] + (t - tst[lo]) * rpt;
+            info = int4{lo, row0, min(rpt, off[lo + 1] - row0), 0};
+        }
+        tile_info[t] = info;
+    }
+}
+
+hipError_t launch_perm_small(const int32_t* ids, int32_t* offsets, int32_t* sorted_token, int32_t* row_of_slot,
+                             int32_t* tile_start, int4* tile_info, int64_t N, int E, int k, int rows_per_tile,
+                             int max_tiles, hipStream_t stream) {
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(kPermBlock), 0, stream, ids, offsets, sorted_token,
+                       row_of_slot, tile_start, tile_info, (int)N, E, k, rows_per_tile, max_tiles);
+    return hipGetLastError();
+}
+
 hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
                              hipStream_t stream) {
     const int nblk = (int)((N + kPermBlock - 1) / kPermBlock);

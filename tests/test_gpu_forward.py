@@ -63,7 +63,9 @@ SMALL = [("tiny", {}, False), ("tiny", dict(bias="zipf", E=32, k=4, T=100), Fals
          # packed weights: streaming and tiled kernels
          ("tiny", dict(T=129, H=512, I=256, E=24, k=8), True), ("tiny", dict(T=40, H=1024, I=640, E=12, k=3), True),
          ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), True),
-         ("tiny", dict(T=400, H=1024, I=1536, E=16, k=8), True)]
+         ("tiny", dict(T=400, H=1024, I=1536, E=16, k=8), True),
+         # at most 1024 slots (single-workgroup permutation) on the tiled kernel
+         ("tiny", dict(T=100, H=512, I=512, E=8, k=4), True)]
 
 
 @pytest.mark.parametrize("cfg,over,packed", SMALL)
