@@ -198,7 +198,10 @@ moe_status moe_combine(const moe_problem* problem, const float* y_perm, const in
                        const float* topk_w, void* y, int32_t out_dtype, hipStream_t stream);
 
 /* The whole layer: moe_route, moe_permute, moe_grouped_gemm_swiglu and
- * moe_combine in one stream, all intermediates in the workspace.          */
+ * moe_combine in one stream, all intermediates in the workspace.  The FP8
+ * gather is fused into the gate/up GEMM (x is quantised once per token and
+ * read through the permutation), which gives the same values as the staged
+ * path.                                                                   */
 moe_status moe_forward(const moe_problem* problem, const void* x_bf16, const void* w_router_bf16,
                        const float* sel_bias, const moe_expert_weights* weights, void* y,
                        int32_t out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -115,7 +115,7 @@ bool use_tiled(const moe_problem& p);
 // workspace; *planned tells the caller that it may skip the plan.
 moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, int32_t* offsets,
                        int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, uint8_t* xs, void* ws,
-                       hipStream_t stream, bool* planned = nullptr) {
+                       hipStream_t stream, bool* planned = nullptr, bool fuse_gather = false) {
     const Layout L = layout_of(p);
     const int64_t N = p.num_tokens * p.top_k;
     if (N <= kPermBlock) {
@@ -133,7 +133,12 @@ moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, 
                                        stream));
         if (planned) *planned = false;
     }
-    MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens, stream));
+    // fused gather: quantise the T tokens once; GEMM-1 reads them through sorted_token
+    if (fuse_gather)
+        MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, nullptr, xq, xs, p.num_tokens, p.hidden, p.num_tokens,
+                                       stream));
+    else
+        MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens, stream));
     return MOE_OK;
 }
 
@@ -142,6 +147,7 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_
                    uint8_t* out_scale) {
     GemmArgs a;
     a.act = act; a.act_scale = act_scale; a.offsets = offsets; a.tile_start = tile_start; a.tile_info = tile_info;
+    a.act_rows = nullptr;
     a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = out_scale;
     a.packed = 0;
     a.N = p.num_tokens * p.top_k;
@@ -164,7 +170,7 @@ moe_status launch_gemm(const moe_problem& p, GemmMode mode, const GemmArgs& a, h
 
 moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, const uint8_t* xs,
                      const int32_t* offsets, const moe_expert_weights& wt, void* out, uint8_t* out_scale,
-                     void* ws, bool plan, hipStream_t stream) {
+                     void* ws, bool plan, hipStream_t stream, const int32_t* act_rows = nullptr) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
     int4* ti = at<int4>(ws, L.tile_info);
@@ -174,6 +180,7 @@ moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, con
                                     max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
     GemmArgs a = gemm_args(p, xq, xs, offsets, ts, ti, wt.w13, wt.w13_scale, out, out_scale);
     a.packed = wt.layout == MOE_WEIGHTS_PACKED;
+    a.act_rows = act_rows;
     return launch_gemm(p, mode, a, stream);
 }
 
@@ -337,9 +344,11 @@ moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_r
     uint8_t* hs = at<uint8_t>(ws, L.hs);
     float* y_perm = at<float>(ws, L.y_perm);
     MOE_CHECK(run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, ids, w, stream));
+    // the FP8 gather is fused into GEMM-1: x is quantised once per token (T rows
+    // instead of T*k) and GEMM-1 reads its rows through sorted_token
     bool planned = false;
-    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream, &planned));
-    MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq, xs, offsets, *weights, hq, hs, ws, !planned, stream));
+    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream, &planned, true));
+    MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq, xs, offsets, *weights, hq, hs, ws, !planned, stream, st));
     MOE_CHECK(run_gemm2(*p, hq, hs, offsets, *weights, y_perm, ws, false, stream));
     MOE_LAUNCH(launch_combine(y_perm, ros, w, y, out_dtype == MOE_OUT_BF16, p->num_tokens, p->hidden, p->top_k,
                               stream));

@@ -172,7 +172,9 @@ __device__ __forceinline__ void stage_scales_issue(const GemmArgs& a, int e, int
     const int i = 64 * wave + lane;                         // 64 dwords per load, 16 * n4 in all
     if (i < 16 * n4) {
         const int rr = i / n4, c = i - rr * n4;
-        const uint8_t* src = a.act_scale + (size_t)(row0 + min(rr, nrows - 1)) * XB + 4 * c;
+        int srow = row0 + min(rr, nrows - 1);
+        if (a.act_rows) srow = a.act_rows[srow];
+        const uint8_t* src = a.act_scale + (size_t)srow * XB + 4 * c;
         __builtin_amdgcn_global_load_lds(src, (lds_void*)(stream_smem + 256 * SB + 256 * wave), 4, 0, 0);
     }
 }
@@ -213,7 +215,8 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         P.s[j] = a.w_scale + row * sstride;
     }
     const int gshift = 8 * g;
-    const int arow = row0 + min(r, nrows - 1);
+    int arow = row0 + min(r, nrows - 1);
+    if (a.act_rows) arow = a.act_rows[arow];
     P.x = a.act + (size_t)arow * K + 16 * g;
     P.xs = a.act_scale + (size_t)arow * (K / kFp8Block);
     if constexpr (SL) {

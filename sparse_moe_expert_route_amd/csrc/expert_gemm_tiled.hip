@@ -107,6 +107,7 @@ struct WStage {
 struct TileCtx {
     const uint8_t* act;        // FP8 activations [N][K]
     const uint8_t* act_scale;  // [N][K/128]
+    const int32_t* act_rows;   // activation row of each expert-ordered row, or null (identity)
     const uint8_t* wp;         // this lane's weight bytes at k = 0
     const uint8_t* wscale;     // the expert's weight scales [rows][K/32]
     int wstage, wstep;         // byte strides of wp per stage and per step
@@ -152,7 +153,9 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4],
     // activation scales: 128 rows x XB bytes, 64 dwords per load
     for (int m = wave; m < XB / 2; m += kWaves) {
         const int i = 64 * m + lane, row = i / (XB / 4), col = i - row * (XB / 4);
-        dma4(c.act_scale + (size_t)(row0 + min(row, nrows - 1)) * XB + 4 * col, xsc + 256 * m);
+        int srow = row0 + min(row, nrows - 1);
+        if (c.act_rows) srow = c.act_rows[srow];
+        dma4(c.act_scale + (size_t)srow * XB + 4 * col, xsc + 256 * m);
     }
     const int R = 32 * wave + r;                        // this lane's LDS weight-scale row
     const int rmod = R % n16;
@@ -162,6 +165,14 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4],
 #pragma unroll
         for (int s = 0; s < 4; ++s) ws.w[s] = *(const uint4*)(wp + st * c.wstage + s * c.wstep);
     };
+
+    // activation row of each of this lane's four stage pieces (fixed for the item)
+    int arow[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        arow[p] = row0 + min(16 * wave + 4 * p + (lane >> 4), nrows - 1);
+        if (c.act_rows) arow[p] = c.act_rows[arow[p]];
+    }
 
     // activation stage: 128 rows x 256 bytes.  Wave w moves rows 16w .. 16w+15,
     // four rows (64 lanes x 16 bytes) per instruction; lane i of an instruction
@@ -173,8 +184,7 @@ __device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4],
         for (int p = 0; p < 4; ++p) {
             const int row = 16 * wave + 4 * p + (lane >> 4);
             const int chunk = (lane & 15) ^ (row & 15);
-            const int rr = row0 + min(row, nrows - 1);
-            dma16(c.act + (size_t)rr * K + st * kStageK + 16 * chunk, lds + (16 * wave + 4 * p) * kStageK);
+            dma16(c.act + (size_t)arow[p] * K + st * kStageK + 16 * chunk, lds + (16 * wave + 4 * p) * kStageK);
         }
     };
 
@@ -323,7 +333,7 @@ __global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmA
             wrow = (r < 16) ? f0 + r : a.I + f0 + (r - 16);
         }
         TileCtx c;
-        c.act = a.act; c.act_scale = a.act_scale;
+        c.act = a.act; c.act_scale = a.act_scale; c.act_rows = a.act_rows;
         const size_t erow = (size_t)e * wrows + wrow;
         if constexpr (PACKED) {
             // 16-row group of the row, K/128 blocks of 1 KB: lane (g, r) takes

@@ -99,6 +99,8 @@ enum GemmMode { kGemm1Swiglu = 0, kGemm1Preact = 1, kGemm2 = 2 };
 struct GemmArgs {
     const uint8_t* act;        // [N][K] e4m3
     const uint8_t* act_scale;  // [N][K/128] e8m0
+    const int32_t* act_rows;   // optional: activation row of each expert-ordered row (gather fused into
+                               // the GEMM: act/act_scale then hold one row per token); null = identity
     const int32_t* offsets;    // [E+1]
     const int32_t* tile_start; // [E+1], tiles of kRowsPerTile rows
     const int4* tile_info;     // per m-tile {expert, first row, rows}, expert -1 past the end

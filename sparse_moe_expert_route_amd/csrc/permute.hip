@@ -222,7 +222,8 @@ hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, co
 }
 
 // ---------------------------------------------------------------------------
-// Quantise + gather: row r of the output is FP8(x[sorted_token[r]]).
+// Quantise + gather: row r of the output is FP8(x[sorted_token[r]]), or
+// FP8(x[r]) without sorted_token (the gather then happens in GEMM-1).
 // 256 threads per row, 8 channels (one 16-byte bf16 load) per thread, so a
 // 128-channel block is 16 consecutive lanes: amax by xor-shuffles within the
 // 16, then the shared block exponent, then RNE e4m3 codes of x * 2^-e
@@ -233,7 +234,8 @@ __global__ void __launch_bounds__(256) quant_gather_kernel(const uint16_t* __res
                                                            uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
                                                            int N, int H, int T) {
     for (int r = blockIdx.x; r < N; r += gridDim.x) {
-        const int t = min(max(sorted_token[r], 0), T - 1);   // rows left unfilled by invalid ids stay in bounds
+        // (no sorted_token: quantise the tokens in their own order)
+        const int t = sorted_token ? min(max(sorted_token[r], 0), T - 1) : r;   // rows left unfilled by invalid ids stay in bounds
         const uint16_t* xr = x + (size_t)t * H;
         uint8_t* qr = xq + (size_t)r * H;
         for (int c = threadIdx.x * 8; c < H; c += 256 * 8) {
