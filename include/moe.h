@@ -57,10 +57,15 @@ typedef enum {
     MOE_ERR_HIP = 4
 } moe_status;
 
-/* How combine weights are derived from the router logits.
- * MOE_SCORE_SOFTMAX_TOPK: softmax over the k selected logits (the measured
- * workloads).  Selection key = L + b (fp32 add), b optional. */
-typedef enum { MOE_SCORE_SOFTMAX_TOPK = 0 } moe_score_func;
+/* How experts are scored, selected and weighted (b = optional selection bias).
+ * MOE_SCORE_SOFTMAX_TOPK: key = L + b (fp32 add); weights = softmax over the
+ *   k selected logits L (the measured workloads).
+ * MOE_SCORE_SIGMOID_BIAS: s = sigmoid(L) = 1 / (1 + e^-L) in fp32;
+ *   key = s + b (fp32 add); weights = the k selected s divided by their sum
+ *   (teardown "How Big Is Each Expert?": experts scored with a sigmoid plus a
+ *   small per-expert correction bias that keeps the load spread).
+ * In both, b steers only the selection, ties go to the lower expert id.  */
+typedef enum { MOE_SCORE_SOFTMAX_TOPK = 0, MOE_SCORE_SIGMOID_BIAS = 1 } moe_score_func;
 
 typedef enum { MOE_OUT_F32 = 0, MOE_OUT_BF16 = 1 } moe_out_dtype;
 
@@ -133,7 +138,7 @@ moe_status moe_prepack_weights(const moe_problem* problem, const moe_expert_weig
  *                         exact bf16 products) when x and w_router are given;
  *                         INPUT when both are NULL (selection on given logits)
  *   topk_ids      [T][k]  int32 out, descending key order, ties -> lower id
- *   topk_w        [T][k]  fp32 out, softmax over the selected logits        */
+ *   topk_w        [T][k]  fp32 out, combine weights per problem->score_func */
 moe_status moe_route(const moe_problem* problem, const void* x_bf16, const void* w_router_bf16,
                      const float* sel_bias, float* logits, int32_t* topk_ids, float* topk_w,
                      hipStream_t stream);

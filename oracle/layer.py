@@ -17,8 +17,9 @@ What the layer is (the pages, by section):
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
   * combine weights are a softmax over the k selected router logits (the
-    measured workload); the selection key may carry an additive per-expert
-    bias that does not enter the weights;
+    measured workload) or, with layer["score"] == "sigmoid", the selected
+    sigmoid scores over their sum; the selection key may carry an additive
+    per-expert bias that does not enter the weights;
   * ties in the selection key go to the lower expert id, -0 equals +0;
   * the expert is SwiGLU: h = silu(gate) * up, silu(z) = z / (1 + exp(-z));
   * W13 stores the I gate rows first, then the I up rows;
@@ -41,6 +42,7 @@ from . import formats as F
 __all__ = [
     "router_logits",
     "select_topk",
+    "sigmoid_scores",
     "permutation",
     "quantize_activations",
     "expert_ffn",
@@ -58,15 +60,29 @@ def router_logits(x_bits, w_router_bits):
     return x @ w.T
 
 
-def select_topk(logits, k, bias=None):
+def sigmoid_scores(logits):
+    """Sigmoid expert scores s = 1 / (1 + exp(-L)) in float64 (teardown "How
+    Big Is Each Expert?": the router scores experts with a sigmoid)."""
+    L = np.asarray(logits, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-L))
+
+
+def select_topk(logits, k, bias=None, score="softmax"):
     """Top-k expert selection and combine weights for every token.
 
-    The selection key is the float32 sum of the float32 logit and the float32
-    selection bias (an IEEE binary32 addition).  The k largest keys are taken
-    in descending order; equal keys go to the lower expert id (a stable sort
-    of the negated keys); -0 and +0 compare equal.  The weights are a softmax
-    over the k selected *unbiased* logits, computed in float64 with the
-    maximum subtracted.
+    score="softmax" (the measured workloads): the selection key is the
+    float32 sum of the float32 logit and the float32 selection bias (an IEEE
+    binary32 addition); the weights are a softmax over the k selected
+    *unbiased* logits, computed in float64 with the maximum subtracted.
+
+    score="sigmoid" (teardown "How Big Is Each Expert?": a sigmoid score plus
+    a small per-expert correction bias): s = sigmoid(L) rounded to float32;
+    the key is the float32 sum s + b; the weights are the k selected scores
+    (float64) divided by their sum.
+
+    In both, the k largest keys are taken in descending order; equal keys go
+    to the lower expert id (a stable sort of the negated keys); -0 and +0
+    compare equal.
 
     logits: [T, E] float32 (or anything castable to it)
     returns (ids [T, k] int32, w [T, k] float64)
@@ -75,12 +91,22 @@ def select_topk(logits, k, bias=None):
     T, E = L.shape
     if not 1 <= k <= E:
         raise ValueError("k must lie in [1, E]")
-    key = L if bias is None else (L + np.asarray(bias, dtype=np.float32)[None, :])
+    if score == "softmax":
+        base = L
+    elif score == "sigmoid":
+        s64 = sigmoid_scores(L)
+        base = s64.astype(np.float32)
+    else:
+        raise ValueError("unknown score function %r" % (score,))
+    key = base if bias is None else (base + np.asarray(bias, dtype=np.float32)[None, :])
     key = key.astype(np.float32)
     order = np.argsort(-key, axis=1, kind="stable")
     ids = order[:, :k].astype(np.int32)
-    sel = np.take_along_axis(L, ids, axis=1).astype(np.float64)
-    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    if score == "softmax":
+        sel = np.take_along_axis(L, ids, axis=1).astype(np.float64)
+        z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    else:
+        z = np.take_along_axis(s64, ids, axis=1)
     w = z / z.sum(axis=1, keepdims=True)
     return ids, w
 
@@ -177,7 +203,7 @@ def forward(layer, logits=None, keep_intermediates=True):
     E = layer["w13"].shape[0]
     L64 = router_logits(x, layer["w_router"])
     L = L64.astype(np.float32) if logits is None else np.asarray(logits, dtype=np.float32)
-    ids, w = select_topk(L, k, layer.get("bias"))
+    ids, w = select_topk(L, k, layer.get("bias"), layer.get("score", "softmax"))
     perm = permutation(ids, E)
     xq, xs = quantize_activations(x)
     st = perm["sorted_token"]
@@ -227,7 +253,7 @@ def forward_tokens(layer, tokens, logits=None):
     x = layer["x"][tokens]
     L64 = router_logits(x, layer["w_router"])
     L = L64.astype(np.float32) if logits is None else np.asarray(logits, dtype=np.float32)
-    ids, w = select_topk(L, k, layer.get("bias"))
+    ids, w = select_topk(L, k, layer.get("bias"), layer.get("score", "softmax"))
     xq, xs = quantize_activations(x)
     a = F.dequantize_fp8_blocks(xq, xs)
     n, H = x.shape

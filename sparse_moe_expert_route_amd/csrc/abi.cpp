@@ -30,7 +30,7 @@ moe_status check_problem(const moe_problem* p) {
     if (p->intermediate <= 0 || p->intermediate % kFp8Block) return MOE_ERR_INVALID_ARGUMENT;
     if (p->num_experts < 1 || p->num_experts > 512) return MOE_ERR_INVALID_ARGUMENT;
     if (p->top_k < 1 || p->top_k > 8 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARGUMENT;
-    if (p->score_func != MOE_SCORE_SOFTMAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (p->score_func != MOE_SCORE_SOFTMAX_TOPK && p->score_func != MOE_SCORE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
     if (p->num_tokens * (int64_t)p->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -104,7 +104,8 @@ moe_status run_route(const moe_problem& p, const void* x, const void* wr, const 
                      int32_t* ids, float* w, hipStream_t stream) {
     if (x) MOE_LAUNCH(launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, logits, p.num_tokens, p.hidden,
                                            p.num_experts, stream));
-    MOE_LAUNCH(launch_topk(logits, bias, ids, w, p.num_tokens, p.num_experts, p.top_k, stream));
+    MOE_LAUNCH(launch_topk(logits, bias, ids, w, p.num_tokens, p.num_experts, p.top_k,
+                           p.score_func == MOE_SCORE_SIGMOID_BIAS, stream));
     return MOE_OK;
 }
 

@@ -63,8 +63,8 @@ __device__ __forceinline__ v4f mfma_w4a8(v8i a, v8i b, v4f c, int scale_a, int s
 // ---------------------------------------------------------------------------
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, float* logits,
                                 int64_t T, int H, int E, hipStream_t stream);
-hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w,
-                       int64_t T, int E, int k, hipStream_t stream);
+hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, int64_t T, int E,
+                       int k, int sigmoid, hipStream_t stream);
 
 hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
                              hipStream_t stream);

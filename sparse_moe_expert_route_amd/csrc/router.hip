@@ -272,7 +272,11 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-template <int EJ>
+// SIG: sigmoid scoring (teardown "How Big Is Each Expert?": the router scores
+// experts with a sigmoid and adds a small per-expert correction bias):
+// key = fp32(sigmoid(L) + b), weights = sigmoid of the selected logits over
+// their sum.  Otherwise softmax scoring as above.
+template <int EJ, bool SIG>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits,
                                                     const float* __restrict__ bias,
                                                     int32_t* __restrict__ ids, float* __restrict__ w,
@@ -289,6 +293,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         const int e = lane + 64 * j;
         if (e < E) {
             float l = L[e];
+            if constexpr (SIG) l = 1.0f / (1.0f + expf(-l));   // the score replaces the logit
             float kf = bias ? l + bias[e] : l;
             lv[j] = l;
             key[j] = ((unsigned long long)ordered_key(kf) << 32) | (uint32_t)(~(uint32_t)e);
@@ -317,11 +322,17 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         if (lane == j) { sel = lsel; sid = e; }
     }
 
-    // softmax over the k selected logits held by lanes 0..k-1
-    float m = lane < k ? sel : -__builtin_inff();
+    // softmax over the k selected logits held by lanes 0..k-1, or the
+    // selected sigmoid scores over their sum
+    float z;
+    if constexpr (SIG) {
+        z = lane < k ? sel : 0.0f;
+    } else {
+        float m = lane < k ? sel : -__builtin_inff();
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    float z = lane < k ? expf(sel - m) : 0.0f;
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        z = lane < k ? expf(sel - m) : 0.0f;
+    }
     float s = z;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
@@ -331,12 +342,13 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     }
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, int64_t T, int E,
-                       int k, hipStream_t stream) {
+template <bool SIG>
+static hipError_t launch_topk_score(const float* logits, const float* bias, int32_t* ids, float* w, int64_t T,
+                                    int E, int k, hipStream_t stream) {
     dim3 grid((unsigned)((T + 3) / 4)), block(256);
     const int ej = (E + 63) / 64;
 #define MOE_TOPK_CASE(n) \
-    case n: hipLaunchKernelGGL((topk_kernel<n>), grid, block, 0, stream, logits, bias, ids, w, (int)T, E, k); break;
+    case n: hipLaunchKernelGGL((topk_kernel<n, SIG>), grid, block, 0, stream, logits, bias, ids, w, (int)T, E, k); break;
     switch (ej) {
         MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
         MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
@@ -344,6 +356,12 @@ hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, flo
     }
 #undef MOE_TOPK_CASE
     return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, int64_t T, int E,
+                       int k, int sigmoid, hipStream_t stream) {
+    return sigmoid ? launch_topk_score<true>(logits, bias, ids, w, T, E, k, stream)
+                   : launch_topk_score<false>(logits, bias, ids, w, T, E, k, stream);
 }
 
 }  // namespace moe

@@ -65,7 +65,7 @@ def problem(layer):
     T, H = layer["x"].shape
     E = layer["w13"].shape[0]
     inter = layer["w2"].shape[2] * 2
-    return moe.Problem.make(T, H, inter, E, layer["top_k"])
+    return moe.Problem.make(T, H, inter, E, layer["top_k"], 1 if layer.get("score") == "sigmoid" else 0)
 
 
 def logit_tol(L_ref):
@@ -73,20 +73,28 @@ def logit_tol(L_ref):
     return LOGIT_RTOL * np.maximum(np.abs(L_ref), rms)
 
 
-def key_margin(L_gpu, L_ref, bias=None):
+def _score(L, score):
+    from oracle import layer as OL
+    return OL.sigmoid_scores(L) if score == "sigmoid" else np.asarray(L, np.float64)
+
+
+def key_margin(L_gpu, L_ref, bias=None, score="softmax"):
     """Per-token uncertainty of the float32 selection keys: the measured |L_gpu - L_ref|
-    plus a few float32 roundings (of the logit and of the bias addition)."""
-    key = np.abs(L_ref) + (0.0 if bias is None else np.abs(bias.astype(np.float64))[None, :])
+    (times 1/4, the sigmoid's largest slope, for sigmoid scores) plus a few float32
+    roundings (of the score, of the sigmoid evaluation and of the bias addition)."""
+    key = np.abs(_score(L_ref, score)) + (0.0 if bias is None else np.abs(bias.astype(np.float64))[None, :])
     dev_ = np.max(np.abs(np.asarray(L_gpu, np.float64) - L_ref), axis=1)
+    if score == "sigmoid":
+        dev_ = dev_ / 4 + 4 * np.finfo(np.float32).eps
     return dev_ + 4 * np.finfo(np.float32).eps * np.max(key, axis=1)
 
 
-def unambiguous_tokens(L_ref, k, bias, margin, order=True):
+def unambiguous_tokens(L_ref, k, bias, margin, order=True, score="softmax"):
     """Tokens whose top-k decision is clear of ties by more than 2*margin.
 
     order=True: every adjacent gap among the k+1 largest keys (set and order);
     order=False: only the gap between the k-th and (k+1)-th key (the set)."""
-    key = L_ref + (0.0 if bias is None else bias.astype(np.float64)[None, :])
+    key = _score(L_ref, score) + (0.0 if bias is None else bias.astype(np.float64)[None, :])
     E = key.shape[1]
     srt = -np.sort(-key, axis=1)[:, :min(k + 1, E)]
     if srt.shape[1] <= k:      # k == E: the set is every expert
@@ -193,7 +201,7 @@ def oracle_with_allowance(layer, tokens=None):
     k = int(layer["top_k"])
     x = layer["x"] if tokens is None else layer["x"][np.asarray(tokens)]
     L = OL.router_logits(x, layer["w_router"])
-    ids, w = OL.select_topk(L.astype(np.float32), k, layer.get("bias"))
+    ids, w = OL.select_topk(L.astype(np.float32), k, layer.get("bias"), layer.get("score", "softmax"))
     xq, xs = OL.quantize_activations(x)
     a = F.dequantize_fp8_blocks(xq, xs)
     n, H = x.shape

@@ -48,7 +48,7 @@ def _P(T=64, H=256, I=128, E=8, k=2, sf=0):
 
 
 @pytest.mark.parametrize("bad", [dict(H=100), dict(H=0), dict(I=64), dict(E=0), dict(E=513), dict(k=0),
-                                 dict(k=9), dict(E=4, k=5), dict(T=-1), dict(sf=1)])
+                                 dict(k=9), dict(E=4, k=5), dict(T=-1), dict(sf=2)])
 def test_workspace_size_rejects_invalid_problems(lib, bad):
     args = dict(T=64, H=256, I=128, E=8, k=2, sf=0)
     args.update(bad)
@@ -110,8 +110,8 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(2 * FAKE), vp(2 * FAKE + 256), None) == 1
     assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w0), vp(2 * FAKE), vp(3 * FAKE), None) == 1
     assert lib.moe_prepack_weights(ctypes.byref(pb), ctypes.byref(w), vp(2 * FAKE), vp(3 * FAKE), None) == 1
-    # unsupported scoring function
-    ps = _P(sf=1)
+    # unknown scoring function
+    ps = _P(sf=2)
     assert lib.moe_route(ctypes.byref(ps), None, None, None, vp(FAKE), vp(FAKE), vp(FAKE), None) == 2
 
 

@@ -68,18 +68,26 @@ SMALL = [("tiny", {}, False), ("tiny", dict(bias="zipf", E=32, k=4, T=100), Fals
          ("tiny", dict(T=100, H=512, I=512, E=8, k=4), True)]
 
 
-@pytest.mark.parametrize("cfg,over,packed", SMALL)
+SIGMOID = [("tiny", dict(T=100, E=32, k=4, bias="zipf"), False), ("tiny", dict(T=300, H=512, I=512, E=8, k=4), True),
+           ("flash_decode", dict(T=16, E=32), True)]
+
+
+@pytest.mark.parametrize("cfg,over,packed", SMALL + [(c, dict(o, score="sigmoid"), pk) for c, o, pk in SIGMOID])
 def test_forward_small_parity(moe, cfg, over, packed):
+    over = dict(over)
+    score = over.pop("score", "softmax")
     lay = S.make_layer(cfg, seed=0, **over)
+    lay["score"] = score
     p = problem(lay)
-    log("forward %s %s packed=%s" % (cfg, over, packed))
+    log("forward %s %s score=%s packed=%s" % (cfg, over, score, packed))
     W = weights(lay, packed)
     y = _forward(moe, lay, p, W)
     ref = oracle_with_allowance(lay)
     L_ref = ref["logits"]
     Lg, ids_g, _ = _gpu_logits(moe, lay, p)
     assert np.all(np.abs(Lg - L_ref) <= logit_tol(L_ref))
-    clear = unambiguous_tokens(L_ref, lay["top_k"], lay["bias"], key_margin(Lg, L_ref, lay["bias"]), order=False)
+    clear = unambiguous_tokens(L_ref, lay["top_k"], lay["bias"], key_margin(Lg, L_ref, lay["bias"], score),
+                               order=False, score=score)
     assert np.array_equal(np.sort(ids_g[clear], 1), np.sort(ref["ids"][clear], 1))
     err, share = check_output(y, ref, rows=clear)
     log("  max err / RMS = %.3e on %d/%d tokens; share of elements beyond the plain bar: %.2e"

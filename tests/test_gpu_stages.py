@@ -69,6 +69,37 @@ def test_topk_given_logits_bitexact(moe, T, E, k, kind, bias):
     assert np.array_equal(host(Ld), L)   # input logits untouched
 
 
+# sigmoid scores: the fp32 sigmoid is not reproducible bit for bit across
+# implementations, so the selection is compared exactly only on tokens whose
+# keys are clear of ties by twice the score uncertainty, and checked for
+# validity on the rest; weights against the GPU's own selection
+@pytest.mark.parametrize("T,E,k,kind,bias", [
+    (64, 8, 2, "normal", None), (37, 64, 8, "ties", None), (129, 256, 8, "normal", "zipf"),
+    (70, 384, 8, "normal", "zipf"), (33, 512, 8, "normal", None), (50, 384, 1, "ties", None),
+])
+def test_topk_sigmoid_given_logits(moe, T, E, k, kind, bias):
+    log("topk sigmoid T=%d E=%d k=%d %s bias=%s" % (T, E, k, kind, bias))
+    L = S.tie_logits(T, E, seed=T) if kind == "ties" else S.normal_f32(8, 1000 + E, T * E, 1.3).reshape(T, E)
+    b = S.zipf_bias(E, 4096, seed=1) * np.float32(0.05) if bias == "zipf" else None
+    p = moe.Problem.make(T, 128, 128, E, k, 1)
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    moe.route(p, None, None, None if b is None else dev(b), dev(L), ids, w)
+    torch.cuda.synchronize()
+    ids_g, w_g = host(ids), host(w)
+    checks.check_routing(ids_g, w_g, E)
+    L64 = L.astype(np.float64)
+    margin = key_margin(L64, L64, b, score="sigmoid")
+    ref_ids, _ = OL.select_topk(L, k, b, "sigmoid")
+    clear = unambiguous_tokens(L64, k, b, margin, score="sigmoid")
+    log("  tokens clear of ties: %d / %d" % (clear.sum(), T))
+    assert np.array_equal(ids_g[clear], ref_ids[clear])
+    keys = OL.sigmoid_scores(L64) + (0 if b is None else b.astype(np.float64)[None, :])
+    assert np.all(checks.topk_is_valid(ids_g, keys, margin))
+    sel = OL.sigmoid_scores(np.take_along_axis(L64, ids_g.astype(np.int64), 1))
+    assert np.max(np.abs(w_g - sel / sel.sum(1, keepdims=True))) <= WEIGHT_ATOL
+
+
 # ---------------------------------------------------------------------------
 # router logits vs the float64 oracle, and the routing they produce
 # ---------------------------------------------------------------------------

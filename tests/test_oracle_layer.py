@@ -32,14 +32,17 @@ from oracle import checks
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _brute_topk(L, k, bias=None):
+def _brute_topk(L, k, bias=None, score="softmax"):
     L = np.asarray(L, dtype=np.float32)
     T, E = L.shape
     ids = np.zeros((T, k), dtype=np.int64)
     for t in range(T):
         keys = []
         for e in range(E):
-            key = np.float32(L[t, e]) + (np.float32(0) if bias is None else np.float32(bias[e]))
+            base = np.float32(L[t, e])
+            if score == "sigmoid":   # torch's sigmoid in float64, rounded to float32
+                base = np.float32(torch.sigmoid(torch.tensor(float(L[t, e]), dtype=torch.float64)).item())
+            key = base + (np.float32(0) if bias is None else np.float32(bias[e]))
             key = float(np.float32(key))
             keys.append((-key if key != 0 else 0.0, e))
         keys.sort()
@@ -60,6 +63,34 @@ def test_select_topk_matches_brute_force(syngen):
     for bias in (None, b):
         ids, w = OL.select_topk(L, 8, bias)
         assert np.array_equal(ids, _brute_topk(L, 8, bias))
+
+
+def test_sigmoid_select_topk_matches_brute_force(syngen):
+    rng = np.random.default_rng(5)
+    for T, E, k in [(30, 8, 2), (12, 64, 8), (6, 384, 8)]:
+        L = (2 * rng.standard_normal((T, E))).astype(np.float32)
+        for bias in (None, (0.05 * rng.standard_normal(E)).astype(np.float32)):
+            ids, w = OL.select_topk(L, k, bias, "sigmoid")
+            assert np.array_equal(ids, _brute_topk(L, k, bias, "sigmoid"))
+            checks.check_routing(ids, w, E)
+            # weights: the selected sigmoid scores over their sum (torch's sigmoid)
+            s = torch.sigmoid(torch.from_numpy(np.take_along_axis(L, ids, 1).astype(np.float64))).numpy()
+            assert np.allclose(w, s / s.sum(1, keepdims=True), rtol=1e-14, atol=0)
+    # ties (equal logits, -0/+0) go to the lower id
+    L = syngen.tie_logits(40, 32)
+    ids, _ = OL.select_topk(L, 8, None, "sigmoid")
+    assert np.array_equal(ids, _brute_topk(L, 8, None, "sigmoid"))
+
+
+def test_sigmoid_without_bias_selects_like_softmax():
+    # the sigmoid is increasing: without a bias both scorings pick the same experts
+    # (logits on a grid far coarser than float32 spacing, so no two scores collide)
+    rng = np.random.default_rng(6)
+    L = (rng.permuted(np.tile(np.arange(64), (20, 1)), axis=1) * 0.05 - 1.6).astype(np.float32)
+    ids_s, w_s = OL.select_topk(L, 8, None, "sigmoid")
+    ids_m, w_m = OL.select_topk(L, 8)
+    assert np.array_equal(ids_s, ids_m)
+    assert not np.allclose(w_s, w_m)   # the weights differ
 
 
 def test_select_topk_special_cases():
@@ -93,6 +124,13 @@ def test_selection_bias_does_not_enter_weights():
     big[31] = 100.0
     ids2, _ = OL.select_topk(L, 4, big)
     assert np.all(ids2[:, 0] == 31)
+    # the same with sigmoid scores
+    s0, v0 = OL.select_topk(L, 4, None, "sigmoid")
+    s1, v1 = OL.select_topk(L, 4, bias, "sigmoid")
+    same = np.all(s1 == s0, axis=1)
+    assert same.sum() >= 60 and np.array_equal(v1[same], v0[same])
+    s2, _ = OL.select_topk(L, 4, big, "sigmoid")
+    assert np.all(s2[:, 0] == 31)
 
 
 def _counting_sort(ids, E):
@@ -147,11 +185,12 @@ def _dense_bruteforce(layer):
     E = layer["w13"].shape[0]
     k = layer["top_k"]
     L = (F.decode_bf16(x) @ F.decode_bf16(layer["w_router"]).T).astype(np.float32)
-    ids = _brute_topk(L, k, layer.get("bias"))
+    score = layer.get("score", "softmax")
+    ids = _brute_topk(L, k, layer.get("bias"), score)
     mask = np.zeros((T, E))
     for t in range(T):
         sel = L[t, ids[t]].astype(np.float64)
-        p = np.exp(sel - sel.max())
+        p = torch.sigmoid(torch.from_numpy(sel)).numpy() if score == "sigmoid" else np.exp(sel - sel.max())
         mask[t, ids[t]] = p / p.sum()
     xq, xs = F.quantize_fp8_blocks(F.decode_bf16(x))
     a = F.dequantize_fp8_blocks(xq, xs)
@@ -180,6 +219,17 @@ def test_routed_oracle_equals_dense_bruteforce(syngen, over):
     checks.check_permutation(out["ids"], out["offsets"], out["sorted_token"], out["row_of_slot"])
     checks.check_fp8_blocks(out["xq"], out["xs"])
     checks.check_fp8_blocks(out["hq_perm"], out["hs_perm"])
+
+
+def test_routed_oracle_with_sigmoid_scores_equals_dense_bruteforce(syngen):
+    for bias in ("zero", "zipf"):
+        layer = syngen.make_layer("tiny", seed=7, T=30, E=16, k=4, bias=bias)
+        layer["score"] = "sigmoid"
+        ref = _dense_bruteforce(layer)
+        out = OL.forward(layer)
+        assert np.max(np.abs(out["y"] - ref)) <= 1e-12 * np.abs(ref).max()
+        toks = np.array([0, 7, 29])
+        assert np.max(np.abs(OL.forward_tokens(layer, toks)["y"] - out["y"][toks])) <= 1e-12 * np.abs(ref).max()
 
 
 def test_routed_oracle_with_zipf_bias_equals_dense_bruteforce(syngen):
@@ -237,10 +287,10 @@ def _mutants():
         out["y"] = out["h"] @ F.decode_mxfp4(w2_e, w2_s_e).T
         return out
 
-    def biased_softmax(logits, k, bias=None):
+    def biased_softmax(logits, k, bias=None, score="softmax"):
         L = np.asarray(logits, dtype=np.float32)
         key = L if bias is None else L + np.asarray(bias, dtype=np.float32)
-        return _orig_select(key, k, None)
+        return _orig_select(key, k, None, score)
 
     def nibbles_swapped(packed):
         p = np.asarray(packed, dtype=np.uint8)
