@@ -43,6 +43,11 @@ CONFIGS = {
     "flash_prefill": dict(T=8192, H=4096, E=256, k=8, I=2048, bias="zero"),
     "pro_decode": dict(T=128, H=6144, E=384, k=8, I=2048, bias="zero"),
     "pro_skewed_prefill": dict(T=16384, H=6144, E=384, k=8, I=2048, bias="zipf"),
+    # one GPU's share of a 4-way tensor-parallel layer: I split four ways
+    "flash_decode_tp4": dict(T=64, H=4096, E=256, k=8, I=512, bias="zero"),
+    "pro_decode_tp4": dict(T=128, H=6144, E=384, k=8, I=512, bias="zero"),
+    "flash_prefill_tp4": dict(T=8192, H=4096, E=256, k=8, I=512, bias="zero"),
+    "pro_skewed_prefill_tp4": dict(T=16384, H=6144, E=384, k=8, I=512, bias="zipf"),
 }
 
 # stream ids of the counter-based generator

@@ -138,7 +138,9 @@ def test_staged_entry_points_equal_forward(moe, packed):
 # the benchmarked path (packed weights) on every workload, and canonical
 # weights on one decode and one prefill workload
 FULL = [("tiny", True), ("flash_decode", True), ("pro_decode", True), ("flash_prefill", True),
-        ("pro_skewed_prefill", True), ("flash_decode", False), ("flash_prefill", False)]
+        ("pro_skewed_prefill", True), ("flash_decode", False), ("flash_prefill", False),
+        # one GPU's share of the 4-way tensor-parallel layer (I = 512)
+        ("flash_decode_tp4", True), ("pro_skewed_prefill_tp4", True)]
 
 
 @pytest.mark.timeout(900)
