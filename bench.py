@@ -50,6 +50,33 @@ def parse():
     return ap.parse_args()
 
 
+GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm.hip",
+                "sparse_moe_expert_route_amd/csrc/expert_gemm_tiled.hip",
+                "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3 counter summary
+    (profiles/traffic_<workload>.md: FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None
+    when there is none or the GEMM sources have changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        parts = line.strip().split(": ", 1)
+        if len(parts) == 2 and parts[0] in ("gemm1_hbm_bytes_per_launch", "sources_sha256"):
+            fields[parts[0]] = parts[1].strip()
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(here, f), "rb").read())
+    if fields.get("sources_sha256") != h.hexdigest() or "gemm1_hbm_bytes_per_launch" not in fields:
+        return None
+    return int(fields["gemm1_hbm_bytes_per_launch"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -156,6 +183,7 @@ def main():
         achieved = gemm1_flops / (gemm1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = measured_traffic(args.config) if not args.canonical_weights else None
     tiled = N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= 6144
     roof["kernel"] = ("expert_gemm_tiled_kernel" if tiled else "expert_gemm_stream_kernel") + \
         "<gate/up + SwiGLU + FP8 requant>"
