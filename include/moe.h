@@ -47,7 +47,7 @@ extern "C" {
 /* Same declaration as the HIP runtime's: a stream handle is an opaque pointer. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -86,17 +86,20 @@ typedef struct {
  *   w13_scale [E][2I][H/32]
  *   w2        [E][H][I/2]
  *   w2_scale  [E][H][I/32]                                                */
-/* Layout of the code bytes w13 and w2 (the scales are always as above).
+/* Layout of the code and scale bytes (w13, w13_scale, w2, w2_scale).
  * MOE_WEIGHTS_CANONICAL: row-major as above (the checkpoint's layout).
  * MOE_WEIGHTS_PACKED: the layout moe_prepack_weights writes.  For one
- *   expert's matrix of R rows and K columns (K/2 bytes per row; w13: R = 2I,
- *   K = H; w2: R = H, K = I), rows go in groups of 16 and columns in steps
- *   of 128 (64 bytes).  Group q, step c is a 1024-byte block at byte offset
- *   (q * K/128 + c) * 1024 of the expert's matrix (experts in order, each
- *   the same size as in the canonical layout); in it, bytes
+ *   expert's matrix of R rows and K columns (w13: R = 2I, K = H; w2: R = H,
+ *   K = I), rows go in groups of 16 and columns in steps of 128; experts stay
+ *   in order, each the same size as in the canonical layout.
+ *   Codes (K/2 bytes per row): group q, step c is a 1024-byte block at byte
+ *   offset (q * K/128 + c) * 1024 of the expert's code matrix; in it, bytes
  *   [64c + 16p, 64c + 16p + 16) of row 16q + r (p = 0..3, r = 0..15) sit at
- *   (16p + r) * 16.  Same bytes, reordered so that one 64-lane load covers
- *   whole cache lines.                                                    */
+ *   (16p + r) * 16.
+ *   Scales (K/32 bytes per row): group q, step c is a 64-byte block at byte
+ *   offset (q * K/128 + c) * 64 of the expert's scale matrix; in it, the 4
+ *   scale bytes of row 16q + r for columns [128c, 128c + 128) sit at 4r.
+ *   Same bytes, reordered so that one 64-lane load covers whole cache lines. */
 typedef enum { MOE_WEIGHTS_CANONICAL = 0, MOE_WEIGHTS_PACKED = 1 } moe_weight_layout;
 
 typedef struct {
@@ -117,16 +120,17 @@ const char* moe_status_string(moe_status status);
  * (the maximum over entry points).  Returns 0 for an invalid problem. */
 size_t moe_workspace_size(const moe_problem* problem);
 
-/* Reorder the expert code bytes into MOE_WEIGHTS_PACKED (a permutation of
+/* Reorder the expert weights into MOE_WEIGHTS_PACKED (a permutation of
  * bytes, nothing is rounded).  Meant to run once, when weights are loaded.
- *   weights     canonical layout (layout == MOE_WEIGHTS_CANONICAL); the
- *               scales are not read
- *   w13_packed  [E][2I][H/2] bytes out, w2_packed [E][H][I/2] bytes out;
- *               must not overlap the inputs
- * The packed weights are then passed as {w13_packed, w13_scale, w2_packed,
- * w2_scale, MOE_WEIGHTS_PACKED}.                                          */
+ *   weights           canonical layout (layout == MOE_WEIGHTS_CANONICAL)
+ *   w13_packed        [E][2I][H/2] bytes out, w13_scale_packed [E][2I][H/32],
+ *   w2_packed         [E][H][I/2] bytes out,  w2_scale_packed  [E][H][I/32];
+ *                     16-byte aligned, none overlapping another or an input
+ * The packed weights are then passed as {w13_packed, w13_scale_packed,
+ * w2_packed, w2_scale_packed, MOE_WEIGHTS_PACKED}.                         */
 moe_status moe_prepack_weights(const moe_problem* problem, const moe_expert_weights* weights,
-                               uint8_t* w13_packed, uint8_t* w2_packed, hipStream_t stream);
+                               uint8_t* w13_packed, uint8_t* w13_scale_packed, uint8_t* w2_packed,
+                               uint8_t* w2_scale_packed, hipStream_t stream);
 
 /* Router and top-k selection (teardown, "How Big Is Each Expert?": a router
  * picks 8 experts for each token; "Why Are the V2.6 Files Half the Size of

@@ -105,7 +105,7 @@ def load():
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_workspace_size.restype = sz
     L.moe_workspace_size.argtypes = [P]
-    L.moe_prepack_weights.argtypes = [P, W, vp, vp, vp]
+    L.moe_prepack_weights.argtypes = [P, W, vp, vp, vp, vp, vp]
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_grouped_gemm_swiglu.argtypes = [P, vp, vp, vp, W, vp, vp, sz, vp]
@@ -163,23 +163,24 @@ def alloc_workspace(p, device="cuda"):
     return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
 
 
-def prepack_weights(p, weights, w13_packed=None, w2_packed=None, stream=None):
-    """Reorder canonical expert codes into the packed layout; returns packed ExpertWeights
-    sharing the scale tensors.  Output tensors are allocated unless given."""
+def prepack_weights(p, weights, w13_packed=None, w2_packed=None, w13_scale_packed=None, w2_scale_packed=None,
+                    stream=None):
+    """Reorder canonical expert codes and scales into the packed layout; returns packed
+    ExpertWeights.  Output tensors are allocated unless given."""
     if weights.layout != WEIGHTS_CANONICAL:
         raise ValueError("prepack_weights needs canonical weights")
     weights.check(p)
-    if w13_packed is None:
-        w13_packed = torch.empty_like(weights.w13)
-    if w2_packed is None:
-        w2_packed = torch.empty_like(weights.w2)
-    _check(w13_packed, torch.uint8, tuple(weights.w13.shape), "w13_packed")
-    _check(w2_packed, torch.uint8, tuple(weights.w2.shape), "w2_packed")
+    outs = []
+    for given, src, name in ((w13_packed, weights.w13, "w13_packed"), (w13_scale_packed, weights.w13_scale, "w13_scale_packed"),
+                             (w2_packed, weights.w2, "w2_packed"), (w2_scale_packed, weights.w2_scale, "w2_scale_packed")):
+        t = torch.empty_like(src) if given is None else given
+        _check(t, torch.uint8, tuple(src.shape), name)
+        outs.append(t)
     W = weights.struct()
-    st = load().moe_prepack_weights(ctypes.byref(p), ctypes.byref(W), _ptr(w13_packed), _ptr(w2_packed),
-                                    _stream(stream))
+    st = load().moe_prepack_weights(ctypes.byref(p), ctypes.byref(W), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
+                                    _ptr(outs[3]), _stream(stream))
     _raise("moe_prepack_weights", st)
-    return ExpertWeights(w13_packed, weights.w13_scale, w2_packed, weights.w2_scale, WEIGHTS_PACKED)
+    return ExpertWeights(outs[0], outs[1], outs[2], outs[3], WEIGHTS_PACKED)
 
 
 def route(p, x, w_router, sel_bias, logits, topk_ids, topk_w, stream=None):

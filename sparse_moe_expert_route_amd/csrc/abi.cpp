@@ -159,9 +159,13 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_
 // Weight-streaming kernel when experts get few rows (decode); LDS-tiled
 // kernel when the average expert has at least 32 rows (prefill).  The choice
 // depends on host-known sizes only, so both GEMMs of one call agree on it.
+// The tiled kernel addresses activations with 32-bit offsets: every
+// activation matrix it reads ([T*k][H] or [T][H], [T*k][I]) stays under 2 GiB.
 bool use_tiled(const moe_problem& p) {
-    return tiled_gemm_supported(p.hidden, p.intermediate) &&
-           p.num_tokens * p.top_k >= 32 * (int64_t)p.num_experts;
+    const int64_t rows = p.num_tokens * p.top_k;
+    const int64_t widest = p.hidden > p.intermediate ? p.hidden : p.intermediate;
+    return tiled_gemm_supported(p.hidden, p.intermediate) && rows >= 32 * (int64_t)p.num_experts &&
+           rows * widest < ((int64_t)1 << 31);
 }
 
 moe_status launch_gemm(const moe_problem& p, GemmMode mode, const GemmArgs& a, hipStream_t stream) {
@@ -222,19 +226,26 @@ size_t moe_workspace_size(const moe_problem* p) {
 }
 
 moe_status moe_prepack_weights(const moe_problem* p, const moe_expert_weights* weights, uint8_t* w13_packed,
-                               uint8_t* w2_packed, hipStream_t stream) {
+                               uint8_t* w13_scale_packed, uint8_t* w2_packed, uint8_t* w2_scale_packed,
+                               hipStream_t stream) {
     MOE_CHECK(check_problem(p));
     MOE_CHECK(check_weights(weights));
     if (weights->layout != MOE_WEIGHTS_CANONICAL) return MOE_ERR_INVALID_ARGUMENT;
-    if (!all_aligned(w13_packed, w2_packed)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!all_aligned(w13_packed, w13_scale_packed, w2_packed, w2_scale_packed)) return MOE_ERR_INVALID_ARGUMENT;
     const size_t E = (size_t)p->num_experts, H = (size_t)p->hidden, I = (size_t)p->intermediate;
-    const size_t n13 = E * 2 * I * (H / 2), n2 = E * H * (I / 2);
-    if (overlaps(w13_packed, n13, weights->w13, n13) || overlaps(w13_packed, n13, weights->w2, n2) ||
-        overlaps(w2_packed, n2, weights->w13, n13) || overlaps(w2_packed, n2, weights->w2, n2) ||
-        overlaps(w13_packed, n13, w2_packed, n2))
-        return MOE_ERR_INVALID_ARGUMENT;
+    const uint8_t* in[4] = {weights->w13, weights->w13_scale, weights->w2, weights->w2_scale};
+    const uint8_t* out[4] = {w13_packed, w13_scale_packed, w2_packed, w2_scale_packed};
+    const size_t n[4] = {E * 2 * I * (H / 2), E * 2 * I * (H / 32), E * H * (I / 2), E * H * (I / 32)};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j) {
+            if (overlaps(out[i], n[i], in[j], n[j])) return MOE_ERR_INVALID_ARGUMENT;
+            if (j != i && overlaps(out[i], n[i], out[j], n[j])) return MOE_ERR_INVALID_ARGUMENT;
+        }
+    }
     MOE_LAUNCH(launch_prepack(weights->w13, w13_packed, (int64_t)(E * 2 * I), (int)H, stream));
+    MOE_LAUNCH(launch_prepack_scales(weights->w13_scale, w13_scale_packed, (int64_t)(E * 2 * I), (int)H, stream));
     MOE_LAUNCH(launch_prepack(weights->w2, w2_packed, (int64_t)(E * H), (int)I, stream));
+    MOE_LAUNCH(launch_prepack_scales(weights->w2_scale, w2_scale_packed, (int64_t)(E * H), (int)I, stream));
     return MOE_OK;
 }
 

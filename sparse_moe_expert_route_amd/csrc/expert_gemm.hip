@@ -50,7 +50,7 @@ __device__ __forceinline__ void load_scale_words(const uint8_t* p, uint32_t (&w)
 
 struct Ptrs {
     const uint8_t* w[4];   // this lane's first weight byte of each row-tile
-    const uint8_t* s[4];   // first scale byte of each weight row
+    const uint8_t* s[4];   // first scale byte of each weight row (packed: its first scale dword)
     const uint8_t* x;      // this lane's first activation byte
     const uint8_t* xs;     // first activation scale byte of the row
     uint32_t ls[4];        // LDS byte offset of each weight row's scales (scales staged in LDS)
@@ -59,7 +59,9 @@ struct Ptrs {
 
 // Scales staged in LDS: the workgroup's 256 weight rows (K/32 bytes each),
 // then its 16 activation rows (K/128 bytes each), unpadded, filled by direct
-// global->LDS loads.
+// global->LDS loads.  Weight scales in the layout they have in memory: row
+// by row (canonical) or as the 16 packed 16-row groups one after another
+// (packed: the 4 bytes of row r for 128 columns c at 64 c + 4 r of its group).
 extern __shared__ __attribute__((aligned(16))) uint8_t stream_smem[];
 __host__ __device__ constexpr int stream_lds_bytes(int K) { return 256 * (K / 32) + 16 * (K / 128); }
 
@@ -92,23 +94,36 @@ __device__ __forceinline__ void load_stage_mem(const Ptrs& P, int kk, Stage<S>& 
 constexpr int kStageLoads = 6 * 2;   // load_stage_mem<2, *>
 
 // scales of the stage from LDS (two-step stages)
-template <int S>
+template <int S, bool PK>
 __device__ __forceinline__ void load_stage_lds(const Ptrs& P, int kk, Stage<S>& st) {
     static_assert(S == 2, "LDS-staged scales use two-step stages");
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint2 v = *(const uint2*)(stream_smem + P.ls[j] + kk / 32);   // 8 scale bytes of the stage
-        st.ws[j][0] = v.x; st.ws[j][1] = v.y;
+        if constexpr (PK) {
+            // the two 128-column steps of the stage, 64 bytes apart
+            st.ws[j][0] = *(const uint32_t*)(stream_smem + P.ls[j] + kk / 2);
+            st.ws[j][1] = *(const uint32_t*)(stream_smem + P.ls[j] + kk / 2 + 64);
+        } else {
+            const uint2 v = *(const uint2*)(stream_smem + P.ls[j] + kk / 32);   // 8 scale bytes of the stage
+            st.ws[j][0] = v.x; st.ws[j][1] = v.y;
+        }
     }
     // both steps' activation scale bytes in one 16-bit read; the MFMA picks byte s
     st.xs[0] = *(const uint16_t*)(stream_smem + P.lx + kk / kFp8Block);
 }
 
 // scales of the stage from global memory
-template <int S>
+template <int S, bool PK>
 __device__ __forceinline__ void load_stage_gscales(const Ptrs& P, int kk, Stage<S>& st) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (PK) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) st.ws[j][s] = *(const uint32_t*)(P.s[j] + (kk / 128 + s) * 64);
+        } else {
+            load_scale_words<S>(P.s[j] + kk / 32, st.ws[j]);
+        }
+    }
     // separate byte loads (a relaxed atomic load is never merged with its
     // neighbour, which would need VALU extraction and an early wait)
 #pragma unroll
@@ -119,8 +134,8 @@ template <int S, bool SL, bool PK>
 __device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
     Stage<S> st;
     load_stage_mem<S, PK>(P, kk, st);
-    if constexpr (SL) load_stage_lds<S>(P, kk, st);
-    else load_stage_gscales<S>(P, kk, st);
+    if constexpr (SL) load_stage_lds<S, PK>(P, kk, st);
+    else load_stage_gscales<S, PK>(P, kk, st);
     return st;
 }
 
@@ -154,7 +169,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // The caller waits on the load counter and barriers before reading.
 // Needs K % 512 == 0 and stream_lds_bytes(K) <= 64 KB (at most 15 weight and
 // 4 activation loads per wave).
-template <int MODE>
+template <int MODE, bool PK>
 __device__ __forceinline__ void stage_scales_issue(const GemmArgs& a, int e, int K, int row0, int nrows) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int SB = K / 32, n16 = SB / 16;                   // 16-byte pieces per weight row
@@ -162,11 +177,20 @@ __device__ __forceinline__ void stage_scales_issue(const GemmArgs& a, int e, int
     const uint8_t* base = a.w_scale + (size_t)e * wrows * SB;
     for (int q = 0; q < n16; ++q) {
         const int m = 4 * q + wave;                         // 1 KB piece of the LDS image
-        const int i = 64 * m + lane, R = i / n16, c = i - R * n16;
-        int grow;
-        if constexpr (MODE == kGemm2) grow = min((int)blockIdx.x * 256 + R, wrows - 1);   // rows past H: never read
-        else grow = (R < 128 ? 0 : a.I - 128) + blockIdx.x * 128 + R;
-        __builtin_amdgcn_global_load_lds(base + (size_t)grow * SB + 16 * c, (lds_void*)(stream_smem + 1024 * m), 16, 0, 0);
+        if constexpr (PK) {
+            // image group G (K/2 bytes) is memory group gq, contiguous
+            const int o = 1024 * m + 16 * lane, G = o / (K / 2), off = o - G * (K / 2);
+            int gq;
+            if constexpr (MODE == kGemm2) gq = min((int)blockIdx.x * 16 + G, wrows / 16 - 1);   // past H: never read
+            else gq = (G < 8 ? 0 : a.I / 16 - 8) + blockIdx.x * 8 + G;
+            __builtin_amdgcn_global_load_lds(base + (size_t)gq * (K / 2) + off, (lds_void*)(stream_smem + 1024 * m), 16, 0, 0);
+        } else {
+            const int i = 64 * m + lane, R = i / n16, c = i - R * n16;
+            int grow;
+            if constexpr (MODE == kGemm2) grow = min((int)blockIdx.x * 256 + R, wrows - 1);   // rows past H: never read
+            else grow = (R < 128 ? 0 : a.I - 128) + blockIdx.x * 128 + R;
+            __builtin_amdgcn_global_load_lds(base + (size_t)grow * SB + 16 * c, (lds_void*)(stream_smem + 1024 * m), 16, 0, 0);
+        }
     }
     const int XB = K / kFp8Block, n4 = XB / 4;              // dwords per activation row, 16 rows
     const int i = 64 * wave + lane;                         // 64 dwords per load, 16 * n4 in all
@@ -212,7 +236,9 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         // packed: the row's 16-row group, lane l's 16 bytes at 16 l of each block
         if constexpr (PK) P.w[j] = a.w + (row - r) * wstride + 16 * lane;
         else P.w[j] = a.w + row * wstride + 16 * g;
-        P.s[j] = a.w_scale + row * sstride;
+        // packed scales: the row's group at (row - r) K/32, row r's dword at 4 r of each step
+        if constexpr (PK) P.s[j] = a.w_scale + (row - r) * sstride + 4 * r;
+        else P.s[j] = a.w_scale + row * sstride;
     }
     const int gshift = 8 * g;
     int arow = row0 + min(r, nrows - 1);
@@ -224,7 +250,8 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int lrow = (MODE == kGemm2) ? 64 * wave + 16 * j : (j >> 1) * 128 + 32 * wave + 16 * (j & 1);
-            P.ls[j] = (uint32_t)((lrow + r) * (K / 32));
+            if constexpr (PK) P.ls[j] = (uint32_t)((lrow / 16) * (K / 2) + 4 * r);
+            else P.ls[j] = (uint32_t)((lrow + r) * (K / 32));
         }
         P.lx = (uint32_t)(256 * (K / 32) + r * (K / kFp8Block));
     }
@@ -246,7 +273,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         // the scale copy overlaps the first two stages' weight and activation
         // loads: wait for the copy alone (the load counter retires in order;
         // the two stages issue kStageLoads loads each), then barrier
-        stage_scales_issue<MODE>(a, e, K, row0, nrows);
+        stage_scales_issue<MODE, PK>(a, e, K, row0, nrows);
         __builtin_amdgcn_sched_barrier(0);
         load_stage_mem<S, PK>(P, 0, s0);
         load_stage_mem<S, PK>(P, min(KS, klast), s1);
@@ -255,8 +282,8 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (!live) return;
-        load_stage_lds<S>(P, 0, s0);
-        load_stage_lds<S>(P, min(KS, klast), s1);
+        load_stage_lds<S, PK>(P, 0, s0);
+        load_stage_lds<S, PK>(P, min(KS, klast), s1);
     } else {
         s0 = load_stage<S, SL, PK>(P, 0);
         s1 = load_stage<S, SL, PK>(P, min(KS, klast));

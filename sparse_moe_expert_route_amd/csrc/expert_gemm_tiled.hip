@@ -16,21 +16,27 @@
 // b with physical block 4b + s, so each lane's weight bytes for a stage are 64
 // contiguous bytes of its row and its 4 weight scales one dword (op_sel = s).
 //
-// Work decomposition: an item is (m-tile of 128 rows of one expert, n-block).
-// A workgroup of 8 waves (two per SIMD) computes 128 rows x (128 h-features =
-// 256 W13 rows) for the gate/up GEMM, or 128 rows x 256 output features for
-// the down GEMM; each wave owns one 32-row weight tile and all 128 rows.
-// The activation tile is staged through LDS by direct global->LDS loads
-// (global_load_lds_dwordx4: no staging registers) in a three-buffer ring, with
-// the 16-byte chunk c of row p stored at chunk slot c ^ (p mod 16) so that the
-// 32 rows read by one MFMA operand fetch hit distinct banks; every wave
-// streams its own weight rows straight into registers.  The item's weight and
-// activation scales are copied to LDS once, at its start.
+// Work decomposition: an item is (m-tile of 128 rows of one expert, block of
+// 512 weight rows): 256 features (gate and up rows) of the gate/up GEMM, or
+// 512 output features of the down GEMM.  A workgroup has 4 waves, one per
+// SIMD; each wave owns 4 weight tiles of 32 rows (in registers, loaded
+// straight from memory) and multiplies them with the 4 token tiles of the
+// m-tile (from LDS), so every activation operand read from LDS feeds four
+// MFMAs.  The 256 accumulators of a wave live in the accumulation registers.
 //
-// Weight layouts: canonical (row-major codes) or the 16-row packed layout
+// Pipeline: the activation tile of a stage (128 rows x 256 bytes) is staged
+// by direct global->LDS loads (no staging registers) into a ring of four
+// buffers, three stages ahead, with the 16-byte chunk c of row p stored at
+// chunk slot c ^ (p mod 16) so that the 32 rows read by one operand fetch hit
+// distinct banks; weight codes and scales go one stage ahead into a second
+// register set.  The loads of a stage are spread over the MFMAs of its first
+// two steps.  The pipeline runs across items: the last stages of an item
+// already fetch the first stages of the workgroup's next item.
+//
+// Weight layouts: canonical (row-major codes and scales) or the packed layout
 // written by moe_prepack_weights, in which one load instruction of a wave
-// covers whole 128-byte lines (a third of the address-unit time of the
-// row-strided canonical loads).
+// covers whole 128-byte lines (codes: 8 lines per load instead of 32; scales:
+// the 4 bytes of a lane for one stage sit next to those of the other lanes).
 //
 // The grid is persistent: workgroups on one XCD (block id mod 8) take a
 // contiguous 1/8 of the item list.  Items are grouped by expert; an expert's
@@ -47,10 +53,16 @@ namespace moe {
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTileRows = 128;            // m-tile rows
-constexpr int kStageK = 256;              // K per LDS stage (bytes of an FP8 row)
+constexpr int kStageK = 256;              // K per stage (bytes of an FP8 row)
 constexpr int kMChunk = 4;                // m-tiles of one expert scheduled together
 constexpr int kWaves = 8;                 // waves per workgroup, two per SIMD
+constexpr int kWT = 2;                    // 32-row weight tiles per wave
+constexpr int kTT = kTileRows / 32;       // 32-row token tiles per m-tile
+constexpr int kItemRows = 32 * kWT * kWaves;   // weight rows per item (512)
 constexpr int kMaxK = 6144;               // largest K the LDS scale copies hold
+constexpr int kActDma = kTileRows * kStageK / 1024 / kWaves;   // 1 KB activation loads per wave per stage
+constexpr int kWaveRows = kTileRows / kWaves;   // activation rows each wave stages
+constexpr int kBlkWaves = kFp8Block / (16 * kWT);   // waves holding one 128-feature block (gate/up)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -69,25 +81,42 @@ __device__ __forceinline__ v16f mfma32_w4a8(v8i a, v8i b, v16f c, int scale_a, i
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 0, OPSEL_A, scale_a, 0, scale_b);
 }
 
-// Activation stage ring in LDS: three buffers, declared as separate objects
+// Activation stage ring in LDS: four buffers, declared as separate objects
 // so that the compiler's wait tracking for direct global->LDS loads can tell
 // a buffer being filled from the one being read.
 __shared__ __attribute__((aligned(16))) uint8_t tl_act0[kTileRows * kStageK];
 __shared__ __attribute__((aligned(16))) uint8_t tl_act1[kTileRows * kStageK];
 __shared__ __attribute__((aligned(16))) uint8_t tl_act2[kTileRows * kStageK];
-// the item's weight scales: 256 rows x K/32 bytes, the 16-byte chunks of row
-// R rotated by R (chunk c at slot (c + R) mod K/512), so that the 32 rows of
-// a wave read different banks
-__shared__ __attribute__((aligned(16))) uint8_t tl_wsc[256 * (kMaxK / 32)];
-// the item's activation scales: 128 rows x K/128 bytes, row-major
-__shared__ __attribute__((aligned(16))) uint8_t tl_xsc[kTileRows * (kMaxK / 128)];
+__shared__ __attribute__((aligned(16))) uint8_t tl_act3[kTileRows * kStageK];
+// activation scales of the current and the next item: 128 rows x K/128
+// bytes each, dword-column major (dword c of row p at byte 4 * (128 c + p)),
+// so that one 4-byte load per lane covers a dword column of 64 rows
+constexpr int kXscBytes = kTileRows * (kMaxK / kFp8Block);
+// 4-byte loads per wave that copy one item's activation scales (at most)
+constexpr int kXscLoads = (kMaxK / kFp8Block / 2 + kWaves - 1) / kWaves;
+__shared__ __attribute__((aligned(16))) uint8_t tl_xsc[2 * kXscBytes];
+// per-row maxima of the SwiGLU epilogue
+__shared__ float tl_red[kWaves * kTileRows];
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9
 // encoding, vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-// vector-memory operations one stage issues per wave: 4 activation pieces and
-// 4 weight loads
-constexpr int kStageLoads = 8;
+
+// Weight codes and scales are read with buffer loads: a wave-uniform
+// resource per item (base address in scalar registers), a 32-bit lane offset
+// that stays fixed for the whole kernel, and the stage offset as the scalar
+// offset, so that the loads cost no per-load address registers.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements (gfx9 family)
+__device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7fffffff, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 
 // Workgroup barrier that waits on nothing: the callers first wait for their
 // own direct-to-LDS loads with an explicit vmcnt.  The empty asm statements
@@ -99,333 +128,419 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-struct WStage {
-    uint4 w[4];     // the wave's 32-row weight tile, 4 steps of 16 bytes
+// vector-memory operations a stage issues per wave, in this order: 4 weight
+// scale dwords, 4 weight loads per step, the activation loads
+constexpr int kStageOps = kWT + 4 * kWT + kActDma;
+// waits before the steps of a stage: the step's weights have landed when at
+// most the operations issued after them are outstanding (one stage ahead: the
+// later steps' weights, the activation loads, and the next stage's scales and
+// weights issued by earlier steps of this stage)
+constexpr int kWaitStep0 = 3 * kWT + kActDma;
+constexpr int kWaitStepN = 2 * kWT + kActDma + kWT + kWT;
+static_assert(kWaitStepN == 3 * kWT + kActDma + kWT, "step wait");
+
+// A work item (wave-uniform).
+struct Item {
+    int e, row0, nrows, nblk;
 };
 
-// Per-item state of the stage loop.
-struct TileCtx {
-    const uint8_t* act;        // FP8 activations [N][K]
-    const uint8_t* act_scale;  // [N][K/128]
-    const int32_t* act_rows;   // activation row of each expert-ordered row, or null (identity)
-    const uint8_t* wp;         // this lane's weight bytes at k = 0
-    const uint8_t* wscale;     // the expert's weight scales [rows][K/32]
-    int wstage, wstep;         // byte strides of wp per stage and per step
-    int K, nstage, row0, nrows;
-    int nblk, I, H;
+// Activation rows of one item that this lane loads (with the gather fused,
+// looked up through act_rows).
+struct Rows {
+    int arow[kActDma];     // row of each of the lane's stage loads
+    int xrow;              // row whose scale dwords the lane copies
 };
 
-// The K loop of one item.  The LDS buffers come in as restrict pointers: the
-// compiler then tags every LDS access with the buffer it touches, and its
-// wait tracking for direct global->LDS loads (which would otherwise make each
-// LDS read wait for every such load in flight) lets a buffer be read while
-// the others are being filled.
-template <int MODE, int PF_STEP>
-__device__ __forceinline__ void tile_kloop(const TileCtx& c, v16f (&acc)[4],
-                                           uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
-                                           uint8_t* __restrict__ act2, uint8_t* __restrict__ wsc,
-                                           uint8_t* __restrict__ xsc) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 5, r = lane & 31;
-    const int K = c.K, nstage = c.nstage, row0 = c.row0, nrows = c.nrows;
-    const uint8_t* wp = c.wp;
-    const int SB = K / 32, n16 = K / 512, XB = K / kFp8Block;
-    auto abuf = [&](auto bc) -> uint8_t* {
-        constexpr int B = decltype(bc)::value;
-        if constexpr (B == 0) return act0; else if constexpr (B == 1) return act1; else return act2;
-    };
-
-    // ---- the item's scales into LDS (waited for with the first stage) ----
-    // weight scales: 256 rows of n16 16-byte chunks, 64 chunks per load
-    for (int m = wave; m < 4 * n16; m += kWaves) {
-        const int i = 64 * m + lane, R = i / n16, slot = i - R * n16;
-        const int ch = (slot + n16 - R % n16) % n16;    // the chunk stored at this slot
-        int grow;                                       // the weight row of LDS row R
-        if constexpr (MODE == kGemm2) {
-            grow = min(c.nblk * 256 + R, c.H - 1);
-        } else {
-            const int w = R >> 5, rr = R & 31;
-            grow = (rr < 16 ? 0 : c.I - 16) + c.nblk * 128 + 16 * w + rr;
-        }
-        dma16(c.wscale + (size_t)grow * SB + 16 * ch, wsc + 1024 * m);
-    }
-    // activation scales: 128 rows x XB bytes, 64 dwords per load
-    for (int m = wave; m < XB / 2; m += kWaves) {
-        const int i = 64 * m + lane, row = i / (XB / 4), col = i - row * (XB / 4);
-        int srow = row0 + min(row, nrows - 1);
-        if (c.act_rows) srow = c.act_rows[srow];
-        dma4(c.act_scale + (size_t)srow * XB + 4 * col, xsc + 256 * m);
-    }
-    const int R = 32 * wave + r;                        // this lane's LDS weight-scale row
-    const int rmod = R % n16;
-
-    // the wave's weight tile for stage st: 16 bytes per lane per step
-    auto load_w = [&](WStage& ws, int st) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ws.w[s] = *(const uint4*)(wp + st * c.wstage + s * c.wstep);
-    };
-
-    // activation row of each of this lane's four stage pieces (fixed for the item)
-    int arow[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        arow[p] = row0 + min(16 * wave + 4 * p + (lane >> 4), nrows - 1);
-        if (c.act_rows) arow[p] = c.act_rows[arow[p]];
-    }
-
-    // activation stage: 128 rows x 256 bytes.  Wave w moves rows 16w .. 16w+15,
-    // four rows (64 lanes x 16 bytes) per instruction; lane i of an instruction
-    // fills chunk slot i%16 of row 4p + i/16 with the global chunk that the
-    // swizzle maps there.
-    auto dma_act = [&](auto bufc, int st) {
-        uint8_t* lds = abuf(bufc);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int row = 16 * wave + 4 * p + (lane >> 4);
-            const int chunk = (lane & 15) ^ (row & 15);
-            dma16(c.act + (size_t)arow[p] * K + st * kStageK + 16 * chunk, lds + (16 * wave + 4 * p) * kStageK);
-        }
-    };
-
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-
-    // Three-deep pipeline: stage st+2's activations (into LDS) and weights
-    // (into a third register set) are issued while stage st is multiplied,
-    // so each load has two stages of MFMA work to land.  Buffer and
-    // register set of stage st are st mod 3; the stage loop is unrolled by
-    // three so that every set is a fixed set of registers.  Two waves share
-    // each SIMD and issue their prefetch at different steps (PF_STEP): while
-    // one waits to issue its loads, the other's MFMAs run.
-    WStage w0, w1, w2;
-    auto stage = [&](auto setc, int st, const WStage& wc, WStage& wn) {
-        constexpr int SET = decltype(setc)::value;
-        constexpr int NXT = (SET + 2) % 3;
-        // stage st landed (only stage st+1's loads may still be in flight),
-        // in every wave: then its buffer may be read, and the buffer of
-        // stage st-1, which stage st+2 refills, is no longer read.  Near
-        // the end the prefetch re-reads the last stage into a free buffer,
-        // so the body has no branch and the load count never changes.
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(kStageLoads));
-        lds_barrier();
-        const int sp = min(st + 2, nstage - 1);
-        auto prefetch = [&]() {
-            dma_act(std::integral_constant<int, NXT>{}, sp);
-            load_w(wn, sp);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        if constexpr (PF_STEP == 0) prefetch();
-        const uint8_t* lds = abuf(setc);
-        // scales of the stage: 4 weight-scale bytes of this lane's row
-        // (byte s for step s), one activation-scale byte per row tile
-        int slot = (st >> 1) + rmod;
-        if (slot >= n16) slot -= n16;
-        const int wsv = *(const int*)(wsc + R * SB + 16 * slot + 8 * (st & 1) + 4 * g);
-        int bs[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bs[j] = xsc[(32 * j + r) * XB + 2 * st + g];
-        v8i B[4];
-        auto read_b = [&](v8i (&Bd)[4], int s) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 32 * j + r;
-                const uint4 lo4 = *(const uint4*)(lds + swz(row, 2 * s + g));
-                const uint4 hi4 = *(const uint4*)(lds + swz(row, 8 + 2 * s + g));
-                Bd[j][0] = lo4.x; Bd[j][1] = lo4.y; Bd[j][2] = lo4.z; Bd[j][3] = lo4.w;
-                Bd[j][4] = hi4.x; Bd[j][5] = hi4.y; Bd[j][6] = hi4.z; Bd[j][7] = hi4.w;
-            }
-        };
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if (s == PF_STEP && s > 0) prefetch();
-            // B operands of one MFMA step (the other wave on the SIMD covers
-            // the LDS latency)
-            read_b(B, s);
-            v8i A;
-            A[0] = wc.w[s].x; A[1] = wc.w[s].y; A[2] = wc.w[s].z; A[3] = wc.w[s].w;
-            A[4] = A[5] = A[6] = A[7] = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                switch (s) {
-                    case 0: acc[j] = mfma32_w4a8<0>(A, B[j], acc[j], wsv, bs[j]); break;
-                    case 1: acc[j] = mfma32_w4a8<1>(A, B[j], acc[j], wsv, bs[j]); break;
-                    case 2: acc[j] = mfma32_w4a8<2>(A, B[j], acc[j], wsv, bs[j]); break;
-                    default: acc[j] = mfma32_w4a8<3>(A, B[j], acc[j], wsv, bs[j]); break;
-                }
-            }
-            // keep each step's LDS reads next to their use (hoisting them
-            // all would need every B operand of the stage live)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    dma_act(I0{}, 0);
-    load_w(w0, 0);
-    dma_act(I1{}, min(1, nstage - 1));
-    load_w(w1, min(1, nstage - 1));
-    int st = 0;
-    for (; st + 3 <= nstage; st += 3) {
-        stage(I0{}, st, w0, w2);
-        stage(I1{}, st + 1, w1, w0);
-        stage(I2{}, st + 2, w2, w1);
-    }
-    if (st < nstage) stage(I0{}, st, w0, w2);
-    if (st + 1 < nstage) stage(I1{}, st + 1, w1, w0);
-    // the tail prefetches have landed and every wave is done reading the
-    // ring and the scale copies before the next item refills them
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-    lds_barrier();
+__device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
+    // items of expert e: [NB * tile_start[e], NB * tile_start[e+1]).  Its
+    // m-tiles go in chunks of kMChunk; within a chunk the order is n-block
+    // major, m-tile minor.
+    const int e = a.tile_info[item / NB].x;
+    const int t0 = a.tile_start[e], nt = a.tile_start[e + 1] - t0;
+    const int local = item - NB * t0;
+    const int full = nt / kMChunk;
+    const int chunk = min(local / (kMChunk * NB), full);
+    const int cs = (chunk < full) ? kMChunk : nt - kMChunk * full;
+    const int within = local - kMChunk * NB * chunk;
+    const int nblk = within / cs;
+    const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
+    return Item{e, ti.y, ti.z, nblk};
 }
 
-template <int MODE, bool PACKED>
-__global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmArgs a) {
-    __shared__ float red[kWaves][kTileRows];
-
+// The persistent loop of one workgroup.  LDS buffers come in as restrict
+// pointers: the compiler then tags every LDS access with the buffer it
+// touches, and its wait tracking for direct global->LDS loads lets a buffer
+// be read while the others are being filled.
+template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
+__device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
+                                           uint8_t* __restrict__ act2, uint8_t* __restrict__ act3,
+                                           uint8_t* __restrict__ xsc, float* __restrict__ red) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, r = lane & 31;
 
     const int K = (MODE == kGemm2) ? a.I : a.H;
     const int wrows = (MODE == kGemm2) ? a.H : 2 * a.I;
-    const int NB = (MODE == kGemm2) ? (a.H + 255) / 256 : a.I / 128;
+    const int NB = (MODE == kGemm2) ? a.H / kItemRows : a.I / (kItemRows / 2);
     const int nstage = K / kStageK;
+    const int XB = K / kFp8Block;
 
     const int ntiles = a.tile_start[a.E];
     const int total = ntiles * NB;
     const int xcd = blockIdx.x & 7, per_xcd = gridDim.x >> 3;
-    const int beg = (int)(((long long)total * xcd) >> 3);
     const int end = (int)(((long long)total * (xcd + 1)) >> 3);
+    int item = (int)(((long long)total * xcd) >> 3) + (int)(blockIdx.x >> 3);
+    if (item >= end) return;
 
-    for (int item = beg + (int)(blockIdx.x >> 3); item < end; item += per_xcd) {
-        // items of expert e: [NB * tile_start[e], NB * tile_start[e+1]).  Its
-        // m-tiles go in chunks of kMChunk; within a chunk the order is n-block
-        // major, m-tile minor, so the m-tiles that share a block of weight rows
-        // run together, while a chunk's activations stay in L2 across n-blocks.
-        const int e = a.tile_info[item / NB].x;
-        const int t0 = a.tile_start[e], nt = a.tile_start[e + 1] - t0;
-        const int local = item - NB * t0;
-        const int full = nt / kMChunk;                              // full chunks
-        const int chunk = min(local / (kMChunk * NB), full);
-        const int cs = (chunk < full) ? kMChunk : nt - kMChunk * full;  // tiles in this chunk
-        const int within = local - kMChunk * NB * chunk;
-        const int nblk = within / cs;
-        const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
-        const int row0 = ti.y, nrows = ti.z;
-
-        // weight rows of this wave: one 32-row tile.  Gate/up: rows 0..15 of
-        // the tile are gate features f0 .. f0+15 and rows 16..31 the up rows
-        // of the same features, so each lane ends up holding matching gate
-        // and up values (accumulator elements i and i + 8).
-        int wrow;
-        bool wave_valid = true;
-        const int f0 = nblk * 128 + 16 * wave;
-        if constexpr (MODE == kGemm2) {
-            const int n0 = nblk * 256 + 32 * wave;
-            wave_valid = n0 < a.H;
-            wrow = (wave_valid ? n0 : 0) + r;   // loads stay in bounds; results dropped
-        } else {
-            wrow = (r < 16) ? f0 + r : a.I + f0 + (r - 16);
-        }
-        TileCtx c;
-        c.act = a.act; c.act_scale = a.act_scale; c.act_rows = a.act_rows;
-        const size_t erow = (size_t)e * wrows + wrow;
-        if constexpr (PACKED) {
-            // 16-row group of the row, K/128 blocks of 1 KB: lane (g, r) takes
-            // its 16 bytes of step s of stage st from block 2st + g, at
-            // 16 * (16s + r mod 16)
-            c.wp = a.w + (erow - (r & 15)) * ((size_t)K / 2) + 1024 * g + 16 * (r & 15);
-            c.wstage = 2048; c.wstep = 256;
-        } else {
-            c.wp = a.w + erow * ((size_t)K / 2) + 64 * g;
-            c.wstage = kStageK / 2; c.wstep = 16;
-        }
-        c.wscale = a.w_scale + (size_t)e * wrows * (K / 32);
-        c.K = K; c.nstage = nstage; c.row0 = row0; c.nrows = nrows;
-        c.nblk = nblk; c.I = a.I; c.H = a.H;
-        v16f acc[4];
-        // the two waves of a SIMD (w and w + 4) issue their prefetch half a
-        // stage apart, so that one multiplies while the other waits on the
-        // load queue
-        if (wave < 4) tile_kloop<MODE, 0>(c, acc, tl_act0, tl_act1, tl_act2, tl_wsc, tl_xsc);
-        else tile_kloop<MODE, 2>(c, acc, tl_act0, tl_act1, tl_act2, tl_wsc, tl_xsc);
-
-        // ---- epilogues: lane holds tokens 32j + r and tile rows 8*(i/4) + 4g + (i%4) ----
-        if constexpr (MODE == kGemm2) {
-            if (wave_valid) {
-                const int n0 = nblk * 256 + 32 * wave + 4 * g;
+    // ---- per-lane geometry ----
+    // Weight row of this lane in weight tile 0, relative to the item's first
+    // row; tile t adds TROWS * t.  Gate/up: rows 0..15 of a tile are gate
+    // features and rows 16..31 the up rows of the same features, so each lane
+    // ends up holding matching gate and up values (accumulator elements i and
+    // i + 8).  Down: 32 consecutive output features per tile.
+    constexpr int TROWS = (MODE == kGemm2) ? 32 : 16;
+    const int lrow = (MODE == kGemm2) ? 32 * kWT * wave + r : ((r < 16) ? 0 : a.I) + 16 * kWT * wave + (r & 15);
+    const int rows_per_blk = (MODE == kGemm2) ? kItemRows : kItemRows / 2;
+    // packed codes: 16-row group q, 128-column step c at (q K/128 + c) KB, row
+    // r's 16 bytes of step piece p at 16 (16 p + r); packed scales: group q,
+    // step c at 64 (q K/128 + c), row r's 4 bytes at 4 r
+    const int wlane = PACKED ? (lrow >> 4) * (8 * K) + 1024 * g + 16 * (r & 15) : lrow * (K / 2) + 64 * g;
+    const int slane = PACKED ? (lrow >> 4) * (K / 2) + 64 * g + 4 * (r & 15) : lrow * (K / 32) + 4 * g;
+    constexpr int WST = PACKED ? 2048 : kStageK / 2;   // code bytes per stage
+    constexpr int WSS = PACKED ? 256 : 16;             // code bytes per step
+    constexpr int SST = PACKED ? 128 : 8;              // scale bytes per stage
+    const int WTS = TROWS * (K / 2), STS = TROWS * (K / 32);   // per weight tile
+    // lane offsets of each weight tile's codes and scales within an item
+    uint32_t wl[kWT], sl[kWT];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int rr = 32 * j + r;
-                    if (rr >= nrows) continue;
-                    float* o = (float*)a.out + (size_t)(row0 + rr) * a.H + n0;
+    for (int t = 0; t < kWT; ++t) {
+        wl[t] = wlane + t * WTS;
+        sl[t] = slane + t * STS;
+    }
+    // swizzled chunk of this lane's activation loads (piece p and p + 4 alike)
+    int coff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) coff[p] = 16 * ((lane & 15) ^ ((4 * p + (lane >> 4)) & 15));
+
+    // first weight row of an item (in the expert-major weight matrix)
+    auto wrow0 = [&](const Item& it) -> size_t { return (size_t)it.e * wrows + (size_t)it.nblk * rows_per_blk; };
+    // expert-ordered rows of the lane's stage loads and scale copies
+    auto arow_of = [&](const Item& it, int p) { return it.row0 + min(kWaveRows * wave + 4 * p + (lane >> 4), it.nrows - 1); };
+    auto xrow_of = [&](const Item& it) { return it.row0 + min(64 * (wave & 1) + lane, it.nrows - 1); };
+    // activation rows of an item (fused gather: expert-ordered row ->
+    // activation row through act_rows)
+    auto lookup_rows = [&](const Item& it, Rows& rw) {
+#pragma unroll
+        for (int p = 0; p < kActDma; ++p) rw.arow[p] = GATHER ? a.act_rows[arow_of(it, p)] : arow_of(it, p);
+        rw.xrow = GATHER ? a.act_rows[xrow_of(it)] : xrow_of(it);
+    };
+    // activation scales of an item: dword column c of rows 64 h .. 64 h + 63
+    // per load (h = wave & 1), loads m = wave, wave + kWaves, ... of XB / 2.  A
+    // fixed count, the surplus repeating the last load: the stage bodies stay
+    // free of branches (a branch lets the compiler sink the previous stage's
+    // MFMAs past the barrier).
+    auto dma_xsc = [&](int xrow, uint8_t* dst) {
+#pragma unroll
+        for (int i = 0; i < kXscLoads; ++i) {
+            // past the wave's last load: the last load of the same row half
+            const int m = min(wave + kWaves * i, XB / 2 - 1 - ((XB / 2 - 1 - wave) & 1));
+            dma4(a.act_scale + 4 * (m >> 1) + (uint32_t)(xrow * XB), dst + 256 * m);
+        }
+    };
+    auto abuf = [&](auto bc) -> uint8_t* {
+        constexpr int B = decltype(bc)::value;
+        if constexpr (B == 0) return act0;
+        else if constexpr (B == 1) return act1;
+        else if constexpr (B == 2) return act2;
+        else return act3;
+    };
+    // activation stage st of pieces p0 .. p0+np-1: wave w moves rows 32w ..
+    // 32w+31, four rows (64 lanes x 16 bytes) per load; lane i of a load
+    // fills chunk slot i%16 of row 4p + i/16 with the chunk the swizzle maps
+    // there
+    auto dma_act = [&](auto bc, const int (&arow)[kActDma], int st, int p0, int np) {
+        uint8_t* lds = abuf(bc);
+        const uint8_t* base = a.act + st * kStageK;   // wave-uniform; the lane part fits 32 bits
+#pragma unroll
+        for (int p = p0; p < p0 + np; ++p)
+            dma16(base + (uint32_t)(arow[p] * K + coff[p & 3]), lds + (kWaveRows * wave + 4 * p) * kStageK);
+    };
+
+    v16f acc[kWT][kTT];
+#pragma unroll
+    for (int t = 0; t < kWT; ++t)
+#pragma unroll
+        for (int j = 0; j < kTT; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[t][j][i] = 0.0f;
+
+    // weight codes of the current stage [step][weight tile]: step s is
+    // refilled with the next stage's codes right after its MFMAs are issued;
+    // weight scales of the current and the next stage (byte s for step s)
+    uint4 wreg[4][kWT];
+    uint32_t wsc[2][kWT];
+    Item icur = item_at(a, item, NB);
+    int nitem = item + per_xcd;
+    bool has_next = nitem < end;
+    Item inxt = has_next ? item_at(a, nitem, NB) : icur;
+    Rows cur, nxt;
+    lookup_rows(icur, cur);
+    int xpar = 0;   // which half of tl_xsc holds the current item's scales
+
+    // ---- prologue: scales and the first stages of the first item ----
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    {
+        int arow[kActDma];
+#pragma unroll
+        for (int p = 0; p < kActDma; ++p) arow[p] = cur.arow[p];
+        dma_xsc(cur.xrow, xsc);
+        dma_act(I0{}, arow, 0, 0, kActDma);
+        if constexpr (DA == 3) dma_act(I1{}, arow, 1, 0, kActDma);
+        const rsrc_t rs = make_rsrc(a.w_scale + wrow0(icur) * (K / 32));
+        const rsrc_t rw = make_rsrc(a.w + wrow0(icur) * (K / 2));
+#pragma unroll
+        for (int t = 0; t < kWT; ++t) wsc[0][t] = bload4(rs, sl[t], 0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int t = 0; t < kWT; ++t) wreg[s][t] = bload16(rw, wl[t], s * WSS);
+        if constexpr (DA == 3) dma_act(I2{}, arow, 2, 0, kActDma);
+        else dma_act(I1{}, arow, 1, 0, kActDma);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+
+    // One stage.  KIND 1: the item's first stage (everything it needs has
+    // landed; starts the row lookups of the next item); KIND 2: its second
+    // (starts the copy of the next item's activation scales).  SET: which
+    // weight-scale set the stage reads.
+    auto stage = [&](auto bufc, auto setc, auto kindc, int st) {
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr int SET = decltype(setc)::value;
+        constexpr int KIND = decltype(kindc)::value;
+        constexpr int NBUF = (BUF + DA) % 4;
+        // this stage's activations, scales and first weights have landed in
+        // every wave, and every wave is done with the buffer the prefetch
+        // below refills
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(kWaitStep0));
+        lds_barrier();
+        const uint8_t* lds = abuf(bufc);
+        const uint8_t* xs = xsc + xpar * kXscBytes;
+        // activation scale byte of each token tile (128-channel block 2st + g)
+        const int xb = 2 * st + g;
+        int bs[kTT];
+#pragma unroll
+        for (int j = 0; j < kTT; ++j) bs[j] = xs[4 * ((xb >> 2) * kTileRows + 32 * j + r) + (xb & 3)];
+        v8i B[kTT];
+        auto read_b = [&](int j, int s) {
+            const int row = 32 * j + r;
+            const uint4 lo4 = *(const uint4*)(lds + swz(row, 2 * s + g));
+            const uint4 hi4 = *(const uint4*)(lds + swz(row, 8 + 2 * s + g));
+            B[j][0] = lo4.x; B[j][1] = lo4.y; B[j][2] = lo4.z; B[j][3] = lo4.w;
+            B[j][4] = hi4.x; B[j][5] = hi4.y; B[j][6] = hi4.z; B[j][7] = hi4.w;
+        };
+#pragma unroll
+        for (int j = 0; j < kTT; ++j) read_b(j, 0);
+        if constexpr (KIND == 1) lookup_rows(inxt, nxt);
+        if constexpr (KIND == 2) dma_xsc(nxt.xrow, xsc + (xpar ^ 1) * kXscBytes);
+        // prefetch targets: weights of the next stage, activations DA stages
+        // ahead (past the item's end: the next item's first stages)
+        const bool wcur = st + 1 < nstage;
+        const size_t wr = wcur ? wrow0(icur) : wrow0(inxt);
+        const int wst = wcur ? st + 1 : 0;
+        const rsrc_t rw = make_rsrc(a.w + wr * (K / 2));
+        const rsrc_t rs = make_rsrc(a.w_scale + wr * (K / 32));
+        const bool acur = st + DA < nstage;
+        const int ast = acur ? st + DA : st + DA - nstage;
+        int arow[kActDma];
+#pragma unroll
+        for (int p = 0; p < kActDma; ++p) arow[p] = acur ? cur.arow[p] : nxt.arow[p];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            // step s's weights have landed
+            if (s > 0) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(kWaitStepN));
+                asm volatile("s_nop 0");
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int j = 0; j < kTT; ++j) {
+#pragma unroll
+                for (int t = 0; t < kWT; ++t) {
+                    const uint4 w = wreg[s][t];
+                    const v8i A = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+                    const int sa = (int)wsc[SET][t];
+                    switch (s) {
+                        case 0: acc[t][j] = mfma32_w4a8<0>(A, B[j], acc[t][j], sa, bs[j]); break;
+                        case 1: acc[t][j] = mfma32_w4a8<1>(A, B[j], acc[t][j], sa, bs[j]); break;
+                        case 2: acc[t][j] = mfma32_w4a8<2>(A, B[j], acc[t][j], sa, bs[j]); break;
+                        default: acc[t][j] = mfma32_w4a8<3>(A, B[j], acc[t][j], sa, bs[j]); break;
+                    }
+                }
+                if (s < 3) read_b(j, s + 1);
+                if (s == 0 && j == 0) {
+#pragma unroll
+                    for (int t = 0; t < kWT; ++t) wsc[SET ^ 1][t] = bload4(rs, sl[t], wst * SST);
+                }
+                if (j == kTT - 1) {
+                    // step s is done with its weights: refill them with the next stage's
+#pragma unroll
+                    for (int t = 0; t < kWT; ++t) wreg[s][t] = bload16(rw, wl[t], wst * WST + s * WSS);
+                    if (s == 3) dma_act(std::integral_constant<int, NBUF>{}, arow, ast, 0, kActDma);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // The stages of one item; B0 = ring buffer of its first stage (0, or 2
+    // when the stage count is 2 mod 4 and the item is odd).
+    auto run_item = [&](auto b0c) {
+        constexpr int B0 = decltype(b0c)::value;
+        using S0 = std::integral_constant<int, 0>;
+        using S1 = std::integral_constant<int, 1>;
+        using KN = std::integral_constant<int, 0>;
+        stage(std::integral_constant<int, B0>{}, S0{}, std::integral_constant<int, 1>{}, 0);
+        stage(std::integral_constant<int, (B0 + 1) % 4>{}, S1{}, std::integral_constant<int, 2>{}, 1);
+        int st = 2;
+        for (; st + 4 <= nstage; st += 4) {
+            stage(std::integral_constant<int, (B0 + 2) % 4>{}, S0{}, KN{}, st);
+            stage(std::integral_constant<int, (B0 + 3) % 4>{}, S1{}, KN{}, st + 1);
+            stage(std::integral_constant<int, B0>{}, S0{}, KN{}, st + 2);
+            stage(std::integral_constant<int, (B0 + 1) % 4>{}, S1{}, KN{}, st + 3);
+        }
+        if (st < nstage) {
+            stage(std::integral_constant<int, (B0 + 2) % 4>{}, S0{}, KN{}, st);
+            stage(std::integral_constant<int, (B0 + 3) % 4>{}, S1{}, KN{}, st + 1);
+        }
+    };
+
+    // Epilogue of the current item, then move on to the next; false past the
+    // workgroup's last item.
+    auto finish_item = [&]() -> bool {
+        // ---- epilogue: lane holds tokens 32j + r and tile rows 8*(i/4) + 4g + (i%4) ----
+        const int row0 = icur.row0, nrows = icur.nrows, nblk = icur.nblk;
+        if constexpr (MODE == kGemm2) {
+#pragma unroll
+            for (int j = 0; j < kTT; ++j) {
+                const int rr = 32 * j + r;
+                if (rr >= nrows) continue;
+                float* o = (float*)a.out + (size_t)(row0 + rr) * a.H + nblk * kItemRows + 32 * kWT * wave + 4 * g;
+#pragma unroll
+                for (int t = 0; t < kWT; ++t)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *(v4f*)(o + 8 * q) = v4f{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
-                }
+                        *(v4f*)(o + 32 * t + 8 * q) =
+                            v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2], acc[t][j][4 * q + 3]};
             }
         } else if constexpr (MODE == kGemm1Preact) {
-            // tile row 8q + 4g + i: q = 0, 1 gate features f0 + 8q + 4g + i, q = 2, 3 up
+            // tile row 8q + 4g + i: q = 0, 1 gate features f + 8q + 4g + i, q = 2, 3 up
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kTT; ++j) {
                 const int rr = 32 * j + r;
                 if (rr >= nrows) continue;
                 float* o = (float*)a.out + (size_t)(row0 + rr) * (2 * a.I);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = (q < 2 ? f0 : a.I + f0) + 8 * (q & 1) + 4 * g;
-                    *(v4f*)(o + n) = v4f{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+                for (int t = 0; t < kWT; ++t) {
+                    const int f = nblk * (kItemRows / 2) + 16 * kWT * wave + 16 * t;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = (q < 2 ? f : a.I + f) + 8 * (q & 1) + 4 * g;
+                        *(v4f*)(o + n) = v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2],
+                                             acc[t][j][4 * q + 3]};
+                    }
                 }
             }
         } else {
-            // SwiGLU on matching gate (element i) and up (element i + 8) values,
-            // then FP8 over the workgroup's 128 features of each row
-            float amax[4];
+            // SwiGLU on matching gate (element i) and up (element i + 8)
+            // values, then FP8 over 128 features: waves 2b and 2b + 1 hold
+            // the features of block b of the item
+            float amax[kTT];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kTT; ++j) {
                 float m = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float gv = acc[j][i];
-                    const float h = gv / (1.0f + __expf(-gv)) * acc[j][i + 8];
-                    acc[j][i] = h;
-                    m = fmaxf(m, fabsf(h));
-                }
+                for (int t = 0; t < kWT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float gv = acc[t][j][i];
+                        const float h = gv / (1.0f + __expf(-gv)) * acc[t][j][i + 8];
+                        acc[t][j][i] = h;
+                        m = fmaxf(m, fabsf(h));
+                    }
                 m = fmaxf(m, __shfl_xor(m, 32, 64));
                 amax[j] = m;
             }
             if (g == 0) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) red[wave][32 * j + r] = amax[j];
+                for (int j = 0; j < kTT; ++j) red[wave * kTileRows + 32 * j + r] = amax[j];
             }
             __syncthreads();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kTT; ++j) {
                 const int rr = 32 * j + r;
-                float m = red[0][rr];
+                const int w0 = wave - wave % kBlkWaves;
+                float m = red[w0 * kTileRows + rr];
 #pragma unroll
-                for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w][rr]);
+                for (int w = 1; w < kBlkWaves; ++w) m = fmaxf(m, red[(w0 + w) * kTileRows + rr]);
                 const int ex = fp8_block_exponent(m);
                 if (rr < nrows) {
-                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + f0 + 4 * g;
+                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + nblk * (kItemRows / 2) + 16 * kWT * wave + 4 * g;
 #pragma unroll
-                    for (int qq = 0; qq < 2; ++qq)
-                        *(uint32_t*)(q + 8 * qq) = pack_fp8x4(__builtin_amdgcn_ldexpf(acc[j][4 * qq], -ex),
-                                                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 1], -ex),
-                                                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 2], -ex),
-                                                              __builtin_amdgcn_ldexpf(acc[j][4 * qq + 3], -ex));
-                    if (wave == 0 && g == 0)
-                        a.out_scale[(size_t)(row0 + rr) * (a.I / kFp8Block) + nblk] = (uint8_t)(ex + 127);
+                    for (int t = 0; t < kWT; ++t)
+#pragma unroll
+                        for (int qq = 0; qq < 2; ++qq)
+                            *(uint32_t*)(q + 16 * t + 8 * qq) = pack_fp8x4(
+                                __builtin_amdgcn_ldexpf(acc[t][j][4 * qq], -ex), __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 1], -ex),
+                                __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 2], -ex), __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 3], -ex));
+                    if (wave % kBlkWaves == 0 && g == 0)
+                        a.out_scale[(size_t)(row0 + rr) * (a.I / kFp8Block) + 2 * nblk + wave / kBlkWaves] = (uint8_t)(ex + 127);
                 }
             }
-            __syncthreads();   // red is reused by the next item
         }
+        // stores and the next item's first loads are complete (stores may
+        // finish out of order with loads, so no partial count is safe here)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        if (!has_next) return false;
+#pragma unroll
+        for (int t = 0; t < kWT; ++t)
+#pragma unroll
+            for (int j = 0; j < kTT; ++j)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[t][j][i] = 0.0f;
+        item = nitem;
+        icur = inxt;
+        cur = nxt;
+        xpar ^= 1;
+        nitem = item + per_xcd;
+        has_next = nitem < end;
+        inxt = has_next ? item_at(a, nitem, NB) : icur;
+        return true;
+    };
+
+    // With a stage count of 2 mod 4 consecutive items start at ring buffers 0
+    // and 2, so items go in pairs; the ring position of every stage stays a
+    // compile-time constant either way.
+    if constexpr (PAIR) {
+        for (;;) {
+            run_item(I0{});
+            if (!finish_item()) break;
+            run_item(I2{});
+            if (!finish_item()) break;
+        }
+    } else {
+        do {
+            run_item(I0{});
+        } while (finish_item());
     }
+}
+
+template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
+__global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmArgs a) {
+    tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red);
 }
 
 static int persistent_grid() {
@@ -443,11 +558,28 @@ bool tiled_gemm_supported(int H, int I) {
     return H % 512 == 0 && I % 512 == 0 && H <= kMaxK && I <= kMaxK;
 }
 
+template <int MODE, bool PACKED, bool GATHER>
+static void launch_tiled_variant(const GemmArgs& a, hipStream_t stream) {
+    dim3 grid(persistent_grid()), block(64 * kWaves);
+    const int K = (MODE == kGemm2) ? a.I : a.H;
+    // three stages of activations in flight need at least four stages per item
+    const int nstage = K / kStageK;
+    if (nstage < 4) hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, PACKED, GATHER, 2, true>), grid, block, 0, stream, a);
+    else if (nstage % 4 == 0) hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, PACKED, GATHER, 3, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, PACKED, GATHER, 3, true>), grid, block, 0, stream, a);
+}
+
 template <int MODE>
 static void launch_tiled_mode(const GemmArgs& a, hipStream_t stream) {
-    dim3 grid(persistent_grid()), block(64 * kWaves);
-    if (a.packed) hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((expert_gemm_tiled_kernel<MODE, false>), grid, block, 0, stream, a);
+    // the down GEMM reads its activations in expert order (no gather)
+    constexpr bool kCanGather = MODE != kGemm2;
+    if (kCanGather && a.act_rows) {
+        if (a.packed) launch_tiled_variant<MODE, true, kCanGather>(a, stream);
+        else launch_tiled_variant<MODE, false, kCanGather>(a, stream);
+    } else {
+        if (a.packed) launch_tiled_variant<MODE, true, false>(a, stream);
+        else launch_tiled_variant<MODE, false, false>(a, stream);
+    }
 }
 
 hipError_t launch_expert_gemm_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream) {

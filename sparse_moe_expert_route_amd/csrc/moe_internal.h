@@ -84,6 +84,7 @@ hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, u
 // row, rows a multiple of 16, K a multiple of 128) into the packed weight
 // layout of moe.h (MOE_WEIGHTS_PACKED).
 hipError_t launch_prepack(const uint8_t* src, uint8_t* dst, int64_t rows, int K, hipStream_t stream);
+hipError_t launch_prepack_scales(const uint8_t* src, uint8_t* dst, int64_t rows, int K, hipStream_t stream);
 
 // tile_info[t] = {expert, first row, rows} of m-tile t for t < max_tiles
 // (expert -1 past the last tile); max_tiles = ceil(N / rows_per_tile) + E.

@@ -40,7 +40,7 @@ def host(t):
 
 
 def weights(layer, packed=False):
-    """Device expert weights of a layer; packed=True reorders the codes with moe_prepack_weights."""
+    """Device expert weights of a layer; packed=True reorders codes and scales with moe_prepack_weights."""
     import sparse_moe_expert_route_amd as moe
     W = moe.ExpertWeights(dev(layer["w13"]), dev(layer["w13_s"]), dev(layer["w2"]), dev(layer["w2_s"]))
     if not packed:
@@ -58,6 +58,15 @@ def pack_codes_reference(codes):
     R, KB = codes.shape
     u = codes.reshape(R // 16, 16, KB // 64, 4, 16)        # q, r, c, p, byte
     return np.ascontiguousarray(u.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+def pack_scales_reference(scales):
+    """The packed scale layout of moe.h written out in numpy: scales [R, K/32] uint8 (R % 16 == 0,
+    K % 128 == 0) -> [R * K/32] uint8 with row 16q + r, the 4 bytes of 128-column step c at
+    block (q, c) of 64 bytes, offset 4r."""
+    R, SB = scales.shape
+    u = scales.reshape(R // 16, 16, SB // 4, 4)            # q, r, c, byte
+    return np.ascontiguousarray(u.transpose(0, 2, 1, 3)).reshape(-1)
 
 
 def problem(layer):

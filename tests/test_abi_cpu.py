@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     for st, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"), (4, b"HIP launch failure")]:
         assert lib.moe_status_string(st) == text
     assert lib.moe_status_string(99) == b"unknown status"
@@ -102,14 +102,21 @@ def test_invalid_arguments_rejected_before_launch(lib):
     wl = _w(layout=7)
     assert lib.moe_forward(ctypes.byref(p), vp(FAKE), vp(FAKE), None, ctypes.byref(wl), vp(FAKE), 0, vp(FAKE), big,
                            None) == 1
-    # prepack: source must be canonical; outputs aligned and not overlapping the inputs or each other
+    # prepack: source must be canonical; outputs aligned, non-null and not overlapping the inputs or each other
+    M = 1 << 20
+    outs = [vp(2 * M), vp(3 * M), vp(4 * M), vp(5 * M)]
+
+    def prepack(problem, weights, o):
+        return lib.moe_prepack_weights(ctypes.byref(problem), ctypes.byref(weights), *o, None)
+
     wp = _w(layout=1)
-    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(wp), vp(2 * FAKE), vp(3 * FAKE), None) == 1
-    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(2 * FAKE + 8), vp(3 * FAKE), None) == 1
-    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(FAKE + 16), vp(3 * FAKE), None) == 1
-    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), vp(2 * FAKE), vp(2 * FAKE + 256), None) == 1
-    assert lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w0), vp(2 * FAKE), vp(3 * FAKE), None) == 1
-    assert lib.moe_prepack_weights(ctypes.byref(pb), ctypes.byref(w), vp(2 * FAKE), vp(3 * FAKE), None) == 1
+    assert prepack(p, wp, outs) == 1
+    assert prepack(p, w, [vp(2 * M + 8)] + outs[1:]) == 1          # misaligned
+    assert prepack(p, w, outs[:3] + [None]) == 1                      # null output
+    assert prepack(p, w, [vp(FAKE + 16)] + outs[1:]) == 1           # overlaps the inputs
+    assert prepack(p, w, outs[:1] + [vp(2 * M + 256)] + outs[2:]) == 1   # scales overlap the codes
+    assert prepack(p, w0, outs) == 1
+    assert prepack(pb, w, outs) == 1
     # unknown scoring function
     ps = _P(sf=2)
     assert lib.moe_route(ctypes.byref(ps), None, None, None, vp(FAKE), vp(FAKE), vp(FAKE), None) == 2

@@ -17,7 +17,7 @@ from oracle import checks
 from oracle import formats as F
 from oracle import layer as OL
 from moe_testutil import (dev, host, log, weights, logit_tol, unambiguous_tokens, key_margin, WEIGHT_ATOL, ACC_REL,
-                          h_rounding_allowance, pack_codes_reference)
+                          h_rounding_allowance, pack_codes_reference, pack_scales_reference)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,14 +191,16 @@ def test_prepack_bitexact(moe, H, I, E):
     rng = np.random.default_rng(H + I + E)
     w13 = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
     w2 = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
-    s13 = np.zeros((E, 2 * I, H // 32), np.uint8)
-    s2 = np.zeros((E, H, I // 32), np.uint8)
+    s13 = rng.integers(0, 256, size=(E, 2 * I, H // 32), dtype=np.uint8)
+    s2 = rng.integers(0, 256, size=(E, H, I // 32), dtype=np.uint8)
     p = moe.Problem.make(1, H, I, E, 1)
     Wp = moe.prepack_weights(p, moe.ExpertWeights(dev(w13), dev(s13), dev(w2), dev(s2)))
     torch.cuda.synchronize()
     assert Wp.layout == moe.WEIGHTS_PACKED
     assert np.array_equal(host(Wp.w13).reshape(-1), pack_codes_reference(w13.reshape(E * 2 * I, H // 2)))
     assert np.array_equal(host(Wp.w2).reshape(-1), pack_codes_reference(w2.reshape(E * H, I // 2)))
+    assert np.array_equal(host(Wp.w13_scale).reshape(-1), pack_scales_reference(s13.reshape(E * 2 * I, H // 32)))
+    assert np.array_equal(host(Wp.w2_scale).reshape(-1), pack_scales_reference(s2.reshape(E * H, I // 32)))
 
 
 # Shapes with few rows per expert run the weight-streaming kernel; those with
