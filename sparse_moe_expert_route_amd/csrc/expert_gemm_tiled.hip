@@ -360,6 +360,16 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
+            // The older wave of a SIMD would otherwise take every MFMA issue
+            // slot until it stalls, leaving the younger one to finish the
+            // stage alone; a priority that falls with the step keeps the two
+            // waves of a SIMD within a step of each other.
+            switch (s) {
+                case 0: __builtin_amdgcn_s_setprio(3); break;
+                case 1: __builtin_amdgcn_s_setprio(2); break;
+                case 2: __builtin_amdgcn_s_setprio(1); break;
+                default: __builtin_amdgcn_s_setprio(0); break;
+            }
             // step s's weights have landed
             if (s > 0) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_only(kWaitStepN));
@@ -487,15 +497,23 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
 #pragma unroll
                 for (int w = 1; w < kBlkWaves; ++w) m = fmaxf(m, red[(w0 + w) * kTileRows + rr]);
                 const int ex = fp8_block_exponent(m);
+                // dword d = 4t + 2qq + g of the row's 32 features: lane g holds
+                // d = g, g + 2, g + 4, g + 6; one swap with lane l ^ 32 leaves
+                // lane g with d = 4g .. 4g + 3, 16 contiguous bytes
+                uint32_t dw[kWT][2];
+#pragma unroll
+                for (int t = 0; t < kWT; ++t)
+#pragma unroll
+                    for (int qq = 0; qq < 2; ++qq)
+                        dw[t][qq] = pack_fp8x4(
+                            __builtin_amdgcn_ldexpf(acc[t][j][4 * qq], -ex), __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 1], -ex),
+                            __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 2], -ex), __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 3], -ex));
+                const uint32_t x0 = g ? dw[0][0] : dw[1][0], x1 = g ? dw[0][1] : dw[1][1];
+                const uint32_t y0 = __shfl_xor(x0, 32, 64), y1 = __shfl_xor(x1, 32, 64);
+                const uint4 v = g ? uint4{y0, dw[1][0], y1, dw[1][1]} : uint4{dw[0][0], y0, dw[0][1], y1};
                 if (rr < nrows) {
-                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + nblk * (kItemRows / 2) + 16 * kWT * wave + 4 * g;
-#pragma unroll
-                    for (int t = 0; t < kWT; ++t)
-#pragma unroll
-                        for (int qq = 0; qq < 2; ++qq)
-                            *(uint32_t*)(q + 16 * t + 8 * qq) = pack_fp8x4(
-                                __builtin_amdgcn_ldexpf(acc[t][j][4 * qq], -ex), __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 1], -ex),
-                                __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 2], -ex), __builtin_amdgcn_ldexpf(acc[t][j][4 * qq + 3], -ex));
+                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + nblk * (kItemRows / 2) + 16 * kWT * wave + 16 * g;
+                    *(uint4*)q = v;
                     if (wave % kBlkWaves == 0 && g == 0)
                         a.out_scale[(size_t)(row0 + rr) * (a.I / kFp8Block) + 2 * nblk + wave / kBlkWaves] = (uint8_t)(ex + 127);
                 }
