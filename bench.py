@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--config", default="flash_decode")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens for the CPU oracle (0 = auto)")
     ap.add_argument("--canonical-weights", action="store_true",
                     help="run on the canonical (row-major) weight layout instead of the packed one")
@@ -144,6 +145,29 @@ def main():
     tokens_per_s = T * args.steps / wall
     log("bench: %.3f ms/step, %.0f tokens/s" % (ms_per_step, tokens_per_s))
 
+    # ---- the same step captured once as a HIP graph and replayed (no launch overhead) ----
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            moe.forward(p, x, wr, bias, W, y, ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            moe.forward(p, x, wr, bias, W, y, ws)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        graph = {"ms_per_step": round(gwall / args.steps * 1e3, 4), "value": round(T * args.steps / gwall, 1)}
+        log("bench: graph replay %.3f ms/step" % graph["ms_per_step"])
+        del g
+
     # ---- dominant kernel: gate/up expert GEMM, timed with HIP events on its stream ----
     logits = torch.empty(T, E, device="cuda")
     ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
@@ -208,6 +232,7 @@ def main():
            "config": {"workload": args.config, "T": T, "H": H, "E": E, "k": k, "I": inter, "seed": args.seed,
                       "bias": cfg["bias"]},
            "roofline": roof, "layer": layer,
+           "graph_replay": graph,
            "weight_layout": "canonical" if args.canonical_weights else "packed",
            "prepack_ms": None if prepack_ms is None else round(prepack_ms, 3)}
 

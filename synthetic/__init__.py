@@ -13,6 +13,8 @@ Release?", a 2,048-wide expert middle in "How Big Is Each Expert?"):
   flash_prefill       T=8192,  H=4096, E=256, k=8, I=2048
   pro_decode          T=128,   H=6144, E=384, k=8, I=2048
   pro_skewed_prefill  T=16384, H=6144, E=384, k=8, I=2048, Zipf-like load
+  flash_verify        T=256,   H=4096, E=256, k=8, I=2048  (speculative verify:
+  pro_verify          T=256,   H=6144, E=384, k=8, I=2048   32 sequences x 8 positions)
 
 Distributions: activations N(0,1) rounded to bf16; router weights 0.02*N(0,1)
 rounded to bf16; expert weights 0.02*N(0,1) encoded as MXFP4.  The skewed
@@ -48,6 +50,10 @@ CONFIGS = {
     "pro_decode_tp4": dict(T=128, H=6144, E=384, k=8, I=512, bias="zero"),
     "flash_prefill_tp4": dict(T=8192, H=4096, E=256, k=8, I=512, bias="zero"),
     "pro_skewed_prefill_tp4": dict(T=16384, H=6144, E=384, k=8, I=512, bias="zipf"),
+    # speculative-decoding verify step: a block of 8 positions (one known, seven
+    # drafted) for each of 32 sequences
+    "flash_verify": dict(T=256, H=4096, E=256, k=8, I=2048, bias="zero"),
+    "pro_verify": dict(T=256, H=6144, E=384, k=8, I=2048, bias="zero"),
 }
 
 # stream ids of the counter-based generator

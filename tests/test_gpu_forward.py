@@ -140,7 +140,9 @@ def test_staged_entry_points_equal_forward(moe, packed):
 FULL = [("tiny", True), ("flash_decode", True), ("pro_decode", True), ("flash_prefill", True),
         ("pro_skewed_prefill", True), ("flash_decode", False), ("flash_prefill", False),
         # one GPU's share of the 4-way tensor-parallel layer (I = 512)
-        ("flash_decode_tp4", True), ("pro_skewed_prefill_tp4", True)]
+        ("flash_decode_tp4", True), ("pro_skewed_prefill_tp4", True),
+        # speculative-decoding verify blocks (32 sequences x 8 positions)
+        ("flash_verify", True), ("pro_verify", True)]
 
 
 @pytest.mark.timeout(900)
@@ -180,3 +182,48 @@ def test_forward_full_size_sampled(moe, cfg, packed):
     err, share = check_output(y[toks], ref, rows=clear)
     log("  max err / RMS = %.3e (%d of %d sampled tokens unambiguous); beyond the plain bar: %.2e"
         % (err, clear.sum(), len(toks), share))
+
+
+# ---------------------------------------------------------------------------
+# Graph capture: the whole forward is device work on one stream (no host
+# synchronisation, allocation or memset), so it can be captured once and
+# replayed; every replay must reproduce the eager result bit for bit, also
+# after eager calls that reuse the workspace with other inputs.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,over,packed", [("tiny", dict(T=129, H=512, I=256, E=24, k=8), True),
+                                             ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), True),
+                                             ("tiny", dict(T=100, E=32, k=4), False),
+                                             ("flash_decode", dict(T=64, E=32), True)])
+def test_forward_graph_replay_matches_eager(moe, cfg, over, packed):
+    log("graph replay %s %s packed=%s" % (cfg, over, packed))
+    lay = S.make_layer(cfg, seed=5, **over)
+    other = S.make_layer(cfg, seed=6, experts=False, **over)
+    p = problem(lay)
+    T, H = lay["x"].shape
+    W = weights(lay, packed)
+    ws = moe.alloc_workspace(p)
+    x, wr = dev(lay["x"]), dev(lay["w_router"])
+    b = None if lay["bias"] is None else dev(lay["bias"])
+    x2 = dev(other["x"])
+    y_ref = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    moe.forward(p, x, wr, b, W, y_ref, ws)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_ref)
+    y2 = torch.empty_like(y_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(p, x, wr, b, W, y, ws)      # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.forward(p, x, wr, b, W, y, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        moe.forward(p, x2, wr, b, W, y2, ws)     # eager work on other inputs, same workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), "replay %d differs from the eager forward" % rep
+    assert not torch.equal(y2, y_ref)
