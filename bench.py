@@ -8,12 +8,16 @@ resident in HBM.
 Prints ONE JSON line:
   value        tokens/s of the whole layer (T tokens per step / wall time per step)
   roofline     the dominant kernel (the gate/up expert GEMM), timed with HIP
-               events on the stream it runs on: algorithmic bytes (decode
-               shapes, HBM-bound) or FLOPs (prefill shapes, MFMA-bound) per
-               launch / mean launch duration, against the MI355X peak
+               events on the stream it runs on: algorithmic bytes (below the
+               625 FLOP/byte ridge point: HBM-bound) or FLOPs (above it:
+               MFMA-bound) per launch / mean launch duration, against the
+               MI355X peak; traffic = HBM bytes per launch from the counter
+               summaries in profiles/ while the GEMM sources are unchanged
+  graph_replay the same step captured once as a HIP graph and replayed
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 Workloads: tiny, flash_decode (default), flash_prefill, pro_decode,
-pro_skewed_prefill (see synthetic/__init__.py).
+pro_skewed_prefill, their one-GPU tensor-parallel shares (*_tp4) and the
+speculative-verify blocks flash_verify, pro_verify (see synthetic/__init__.py).
 """
 
 import argparse
@@ -195,11 +199,13 @@ def main():
     torch.cuda.synchronize()
     gemm1_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
 
-    decode = N <= 4 * E   # few rows per expert: the weights dominate the traffic
     w13_bytes_per_expert = 2 * inter * (H // 2 + H // 32)
     gemm1_bytes = touched * w13_bytes_per_expert + N * (H + H // 128) + N * (inter + inter // 128)
     gemm1_flops = 2.0 * N * 2 * inter * H
-    if decode:
+    # the kernel's bound: below the ridge point (peak FLOP/s over peak bytes/s, 625 FLOP/byte)
+    # the weight and activation bytes take longer than the MFMA work
+    ridge = MFMA_FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gemm1_flops / gemm1_bytes < ridge:
         achieved = gemm1_bytes / (gemm1_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
