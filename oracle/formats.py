@@ -12,6 +12,8 @@ table row "Routed experts"; the vLLM recipe, "Overview"):
   * FP8 compute: OCP e4m3 ("FN": bias 7, no infinities, 0x7f/0xff are NaN,
     largest finite 448).
   * BF16 router weights and activations: the top 16 bits of an IEEE binary32.
+  * FP8 block-scaled expert weights (the earlier V2.5 expert format, same
+    table): e4m3 codes, one float32 scale per 128 x 128 block.
 
 Every decoder maps codes to float64 exactly; none rounds.
 """
@@ -28,6 +30,9 @@ __all__ = [
     "encode_e4m3_rne",
     "quantize_fp8_blocks",
     "dequantize_fp8_blocks",
+    "decode_fp8_block",
+    "quantize_fp8_blocks_f32",
+    "dequantize_fp8_blocks_f32",
     "FP8_BLOCK",
     "MX_BLOCK",
     "E4M3_MAX",
@@ -187,3 +192,61 @@ def dequantize_fp8_blocks(codes, scales, block=FP8_BLOCK):
     codes = np.asarray(codes, dtype=np.uint8)
     R, C = codes.shape
     return decode_e4m3(codes) * np.repeat(decode_e8m0(scales), block, axis=-1).reshape(R, C)
+
+
+# ---------------------------------------------------------------------------
+# FP8 block-scaled experts (teardown "Why Are the V2.6 Files Half the Size of
+# V2.5?", table row "Routed experts", V2.5 column: FP8 E4M3 with one F32 scale
+# per 128 x 128 block; vLLM recipe "Overview": computed as block-wise e4m3 at
+# 128 x 128 granularity).
+# ---------------------------------------------------------------------------
+
+def decode_fp8_block(codes, scales, block=FP8_BLOCK):
+    """FP8 block-scaled matrix -> float64.
+
+    codes  [R, K] uint8 e4m3
+    scales [R/128, K/128] float32, one per 128 x 128 block
+    returns [R, K] float64, element (i, j) = e4m3 value * scales[i // 128, j // 128].
+    """
+    vals = decode_e4m3(codes)
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return vals * np.repeat(np.repeat(sc, block, axis=0), block, axis=1)
+
+
+def quantize_fp8_blocks_f32(v, block=FP8_BLOCK):
+    """Dynamic FP8 quantisation of rows with a float32 scale per row per `block` channels.
+
+    The activation scheme that goes with FP8 block-scaled weights.  The pages
+    name the weight format only; the reading used here is the plain
+    amax-over-maximum rule, evaluated in binary32 because the scale is stored
+    as a binary32 and the kernel decides every code in that precision:
+      amax = max |v| over the run (v rounded to binary32 first),
+      s    = amax / 448 (one binary32 division),
+      code = e4m3 round-to-nearest-even of (v / s) (one binary32 division;
+             the quotient can exceed 448 by one binary32 rounding, and any
+             such value rounds to 448).
+    A run with amax == 0 stores s = 0 and the codes of v / 1 (signed zeros).
+
+    v: [R, C] (float64 or float32) with C % block == 0
+    returns (codes [R, C] uint8, scales [R, C/block] float32)
+    """
+    v32 = np.asarray(v).astype(np.float32)
+    R, C = v32.shape
+    if C % block:
+        raise ValueError("channel count must be a multiple of the block")
+    blocks = v32.reshape(R, C // block, block)
+    amax = np.abs(blocks).max(axis=-1)
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    div = np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+    q = (blocks / div[..., None]).astype(np.float32)
+    q = np.clip(q, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    codes = encode_e4m3_rne(q.astype(np.float64)).reshape(R, C)
+    return codes, s
+
+
+def dequantize_fp8_blocks_f32(codes, scales, block=FP8_BLOCK):
+    """e4m3 code value times its run's float32 scale (float64)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    R, C = codes.shape
+    sc = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    return decode_e4m3(codes) * np.repeat(sc, block, axis=-1).reshape(R, C)

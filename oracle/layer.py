@@ -12,7 +12,10 @@ What the layer is (the pages, by section):
     there is no shared expert, so the output is the routed sum alone;
   * teardown "Why Are the V2.6 Files Half the Size of V2.5?": experts are
     stored as MXFP4, the router is BF16;
-  * vLLM recipe "Overview": computed as FP8 e4m3, block-wise.
+  * vLLM recipe "Overview": computed as FP8 e4m3, block-wise;
+  * teardown "Why Are the V2.6 Files Half the Size of V2.5?", V2.5 column:
+    the earlier expert format, FP8 e4m3 with one float32 scale per 128 x 128
+    block (layer["format"] == "fp8_block").
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
@@ -24,7 +27,9 @@ design notes of the repository):
   * the expert is SwiGLU: h = silu(gate) * up, silu(z) = z / (1 + exp(-z));
   * W13 stores the I gate rows first, then the I up rows;
   * activations and h are quantised with one power-of-two (e8m0) scale per
-    row per 128 channels and round-to-nearest-even e4m3 codes;
+    row per 128 channels and round-to-nearest-even e4m3 codes; with FP8
+    block-scaled experts, with one float32 scale amax / 448 per row per 128
+    channels instead (formats.quantize_fp8_blocks_f32);
   * combine weights apply after the down projection, summed in slot order.
 
 Layouts (row-major, "[A, B]" means B contiguous):
@@ -33,6 +38,9 @@ Layouts (row-major, "[A, B]" means B contiguous):
   bias     [E]         float32 (selection only) or None
   w13      [E, 2I, H/2] uint8 MXFP4 codes,   w13_s [E, 2I, H/32] uint8 e8m0
   w2       [E, H, I/2]  uint8 MXFP4 codes,   w2_s  [E, H, I/32]  uint8 e8m0
+  or, with layer["format"] == "fp8_block":
+  w13      [E, 2I, H]   uint8 e4m3 codes,    w13_s [E, 2I/128, H/128] float32
+  w2       [E, H, I]    uint8 e4m3 codes,    w2_s  [E, H/128, I/128]  float32
 """
 
 import numpy as np
@@ -50,7 +58,35 @@ __all__ = [
     "forward",
     "forward_tokens",
     "expert_gate_up",
+    "decode_expert_matrix",
+    "expert_format",
 ]
+
+MXFP4 = "mxfp4"
+FP8_BLOCK = "fp8_block"
+
+
+def expert_format(layer):
+    """The layer's expert weight format: "mxfp4" (default) or "fp8_block"."""
+    fmt = layer.get("format", MXFP4)
+    if fmt not in (MXFP4, FP8_BLOCK):
+        raise ValueError("unknown expert format %r" % (fmt,))
+    return fmt
+
+
+def decode_expert_matrix(codes, scales, fmt=MXFP4):
+    """One expert weight matrix -> float64 [rows, K] in the given storage format."""
+    if fmt == FP8_BLOCK:
+        return F.decode_fp8_block(codes, scales)
+    return F.decode_mxfp4(codes, scales)
+
+
+def _quantize(v, fmt):
+    return F.quantize_fp8_blocks_f32(v) if fmt == FP8_BLOCK else F.quantize_fp8_blocks(v)
+
+
+def _dequantize(codes, scales, fmt):
+    return F.dequantize_fp8_blocks_f32(codes, scales) if fmt == FP8_BLOCK else F.dequantize_fp8_blocks(codes, scales)
 
 
 def router_logits(x_bits, w_router_bits):
@@ -140,9 +176,10 @@ def permutation(ids, num_experts):
     }
 
 
-def quantize_activations(x_bits):
-    """Dynamic FP8 quantisation of the bf16 activations, per token per 128 channels."""
-    return F.quantize_fp8_blocks(F.decode_bf16(x_bits))
+def quantize_activations(x_bits, fmt=MXFP4):
+    """Dynamic FP8 quantisation of the bf16 activations, per token per 128 channels
+    (e8m0 scales with MXFP4 experts, float32 scales with FP8 block-scaled experts)."""
+    return _quantize(F.decode_bf16(x_bits), fmt)
 
 
 def _silu(z):
@@ -150,32 +187,34 @@ def _silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def expert_gate_up(a, w13_e, w13_s_e):
+def expert_gate_up(a, w13_e, w13_s_e, fmt=MXFP4):
     """Pre-activations of one expert: [G | U] = A . W13_e^T in float64.
 
     a: [n, H] float64 (already dequantised activations)
     returns [n, 2I] float64 with columns 0..I-1 = gate, I..2I-1 = up
     """
-    w13 = F.decode_mxfp4(w13_e, w13_s_e)
+    w13 = decode_expert_matrix(w13_e, w13_s_e, fmt)
     return a @ w13.T
 
 
-def expert_ffn(a, w13_e, w13_s_e, w2_e, w2_s_e):
+def expert_ffn(a, w13_e, w13_s_e, w2_e, w2_s_e, fmt=MXFP4):
     """One expert on the rows routed to it.
 
     a: [n, H] float64 dequantised FP8 activations
     returns dict with
       gu  [n, 2I] float64 pre-activations (gate | up)
       h   [n, I]  float64 silu(gate) * up
-      hq, hs      FP8 codes [n, I] and e8m0 scales [n, I/128] of h
+      hq, hs      FP8 codes [n, I] and scales [n, I/128] of h (e8m0 bytes, or
+                  float32 with FP8 block-scaled experts, where h is rounded to
+                  float32 before it is quantised)
       y   [n, H]  float64 down projection of the dequantised h
     """
-    gu = expert_gate_up(a, w13_e, w13_s_e)
+    gu = expert_gate_up(a, w13_e, w13_s_e, fmt)
     inter = gu.shape[1] // 2
     h = _silu(gu[:, :inter]) * gu[:, inter:]
-    hq, hs = F.quantize_fp8_blocks(h)
-    hd = F.dequantize_fp8_blocks(hq, hs)
-    w2 = F.decode_mxfp4(w2_e, w2_s_e)
+    hq, hs = _quantize(h, fmt)
+    hd = _dequantize(hq, hs, fmt)
+    w2 = decode_expert_matrix(w2_e, w2_s_e, fmt)
     return {"gu": gu, "h": h, "hq": hq, "hs": hs, "y": hd @ w2.T}
 
 
@@ -205,23 +244,24 @@ def forward(layer, logits=None, keep_intermediates=True):
     L = L64.astype(np.float32) if logits is None else np.asarray(logits, dtype=np.float32)
     ids, w = select_topk(L, k, layer.get("bias"), layer.get("score", "softmax"))
     perm = permutation(ids, E)
-    xq, xs = quantize_activations(x)
+    fmt = expert_format(layer)
+    xq, xs = quantize_activations(x, fmt)
     st = perm["sorted_token"]
     xq_perm, xs_perm = xq[st], xs[st]
-    a_perm = F.dequantize_fp8_blocks(xq_perm, xs_perm)
+    a_perm = _dequantize(xq_perm, xs_perm, fmt)
     T, H = x.shape
-    inter = layer["w2"].shape[2] * 2
+    inter = layer["w13"].shape[1] // 2
     y_perm = np.zeros((T * k, H), dtype=np.float64)
     gu_perm = np.zeros((T * k, 2 * inter), dtype=np.float64) if keep_intermediates else None
     hq_perm = np.zeros((T * k, inter), dtype=np.uint8)
-    hs_perm = np.zeros((T * k, inter // F.FP8_BLOCK), dtype=np.uint8)
+    hs_perm = np.zeros((T * k, inter // F.FP8_BLOCK), dtype=np.float32 if fmt == FP8_BLOCK else np.uint8)
     off = perm["offsets"]
     for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 == r0:
             continue
         out = expert_ffn(a_perm[r0:r1], layer["w13"][e], layer["w13_s"][e],
-                         layer["w2"][e], layer["w2_s"][e])
+                         layer["w2"][e], layer["w2_s"][e], fmt)
         y_perm[r0:r1] = out["y"]
         hq_perm[r0:r1], hs_perm[r0:r1] = out["hq"], out["hs"]
         if keep_intermediates:
@@ -254,14 +294,15 @@ def forward_tokens(layer, tokens, logits=None):
     L64 = router_logits(x, layer["w_router"])
     L = L64.astype(np.float32) if logits is None else np.asarray(logits, dtype=np.float32)
     ids, w = select_topk(L, k, layer.get("bias"), layer.get("score", "softmax"))
-    xq, xs = quantize_activations(x)
-    a = F.dequantize_fp8_blocks(xq, xs)
+    fmt = expert_format(layer)
+    xq, xs = quantize_activations(x, fmt)
+    a = _dequantize(xq, xs, fmt)
     n, H = x.shape
     y_slot = np.zeros((n, k, H), dtype=np.float64)
     for e in np.unique(ids):
         sel = np.argwhere(ids == e)                     # (row, j) pairs routed to e
         out = expert_ffn(a[sel[:, 0]], layer["w13"][e], layer["w13_s"][e],
-                         layer["w2"][e], layer["w2_s"][e])
+                         layer["w2"][e], layer["w2_s"][e], fmt)
         y_slot[sel[:, 0], sel[:, 1]] = out["y"]
     y = np.zeros((n, H), dtype=np.float64)
     for j in range(k):

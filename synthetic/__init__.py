@@ -15,9 +15,16 @@ Release?", a 2,048-wide expert middle in "How Big Is Each Expert?"):
   pro_skewed_prefill  T=16384, H=6144, E=384, k=8, I=2048, Zipf-like load
   flash_verify        T=256,   H=4096, E=256, k=8, I=2048  (speculative verify:
   pro_verify          T=256,   H=6144, E=384, k=8, I=2048   32 sequences x 8 positions)
+  *_tp4               the same with I=512 (one GPU's share of a 4-way split)
+  *_fp8               the same shapes with FP8 block-scaled experts (e4m3 codes,
+                      one float32 scale per 128 x 128 block: the V2.5 expert
+                      format in the teardown's "Why Are the V2.6 Files Half the
+                      Size of V2.5?" table)
 
 Distributions: activations N(0,1) rounded to bf16; router weights 0.02*N(0,1)
-rounded to bf16; expert weights 0.02*N(0,1) encoded as MXFP4.  The skewed
+rounded to bf16; expert weights 0.02*N(0,1) encoded as MXFP4 (or, with
+format="fp8_block", as e4m3 codes with scale amax/448 per 128 x 128 block,
+from the same normals).  The skewed
 workload adds a selection bias b_e = -0.55 * (0.02*sqrt(H)) * ln(r_e), with
 r a seeded permutation of 1..E, so that expert load falls off roughly as
 rank^-1.1 (a Zipf law, capped at T rows per expert).
@@ -31,7 +38,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS", "config", "make_layer", "zipf_bias", "lib", "build",
-    "philox4x32_10", "normal_f32", "bf16_normal", "mxfp4_normal",
+    "philox4x32_10", "normal_f32", "bf16_normal", "mxfp4_normal", "fp8block_normal",
     "lossless_gemm_inputs", "tie_logits", "random_ids",
 ]
 
@@ -54,6 +61,10 @@ CONFIGS = {
     # drafted) for each of 32 sequences
     "flash_verify": dict(T=256, H=4096, E=256, k=8, I=2048, bias="zero"),
     "pro_verify": dict(T=256, H=6144, E=384, k=8, I=2048, bias="zero"),
+    # FP8 block-scaled experts (the earlier expert format)
+    "flash_decode_fp8": dict(T=64, H=4096, E=256, k=8, I=2048, bias="zero", format="fp8_block"),
+    "pro_decode_fp8": dict(T=128, H=6144, E=384, k=8, I=2048, bias="zero", format="fp8_block"),
+    "flash_prefill_fp8": dict(T=8192, H=4096, E=256, k=8, I=2048, bias="zero", format="fp8_block"),
 }
 
 # stream ids of the counter-based generator
@@ -89,6 +100,7 @@ def lib():
         L.syn_bf16_normal.argtypes = [u64, u64, i64, f32, vp]
         L.syn_mxfp4_normal.argtypes = [u64, u64, i64, i64, f32, vp, vp]
         L.syn_mxfp4_normal_batched.argtypes = [u64, u64, i64, i64, i64, f32, vp, vp]
+        L.syn_fp8block_normal_batched.argtypes = [u64, u64, i64, i64, i64, f32, vp, vp]
         L.syn_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -133,6 +145,17 @@ def mxfp4_normal(seed, stream, rows, K, scale=0.02, batch=None):
     return codes, scales
 
 
+def fp8block_normal(seed, stream, rows, K, scale=0.02, batch=1):
+    """FP8 block-scaled encoding of scale*N(0,1) matrices (the normals of mxfp4_normal with the
+    same arguments): codes [batch, rows, K] uint8 e4m3, scales [batch, rows/128, K/128] float32."""
+    if rows % 128 or K % 128:
+        raise ValueError("rows and K must be multiples of 128")
+    codes = np.empty((batch, rows, K), dtype=np.uint8)
+    scales = np.empty((batch, rows // 128, K // 128), dtype=np.float32)
+    lib().syn_fp8block_normal_batched(seed, stream, batch, rows, K, scale, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
 def config(name_or_cfg, **over):
     cfg = dict(CONFIGS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
     cfg.update(over)
@@ -140,6 +163,7 @@ def config(name_or_cfg, **over):
         cfg.setdefault("name", name_or_cfg)
     cfg.setdefault("name", "custom")
     cfg.setdefault("bias", "zero")
+    cfg.setdefault("format", "mxfp4")
     return cfg
 
 
@@ -161,10 +185,13 @@ def make_layer(name_or_cfg, seed=0, experts=True, **over):
     experts=False skips the expert weights (for router-only uses)."""
     cfg = config(name_or_cfg, **over)
     T, H, E, k, inter = cfg["T"], cfg["H"], cfg["E"], cfg["k"], cfg["I"]
-    layer = dict(cfg=cfg, top_k=k)
+    layer = dict(cfg=cfg, top_k=k, format=cfg["format"])
     layer["x"] = bf16_normal(seed, STREAM_X, (T, H), 1.0)
     layer["w_router"] = bf16_normal(seed, STREAM_WR, (E, H), 0.02)
-    if experts:
+    if experts and cfg["format"] == "fp8_block":
+        layer["w13"], layer["w13_s"] = fp8block_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
+        layer["w2"], layer["w2_s"] = fp8block_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
+    elif experts:
         layer["w13"], layer["w13_s"] = mxfp4_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
         layer["w2"], layer["w2_s"] = mxfp4_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
     if cfg["bias"] == "zipf":

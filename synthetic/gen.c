@@ -1,6 +1,7 @@
 /*
  * Seeded synthetic inputs for the routed MoE layer: bf16 activations and
- * router weights, and MXFP4 expert weights, all drawn from scaled normals.
+ * router weights, and MXFP4 (or FP8 block-scaled) expert weights, all drawn
+ * from scaled normals.
  *
  * This is input synthesis only.  It implements none of the layer's
  * arithmetic: the layer decodes MXFP4 and quantises activations; this file
@@ -25,6 +26,7 @@
 #define _GNU_SOURCE
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -178,6 +180,65 @@ void syn_mxfp4_normal_batched(uint64_t seed, uint64_t stream_base, int64_t E, in
                 }
             }
         }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * FP8 block-scaled weights (input synthesis rule for the e4m3 / 128 x 128
+ * format): for each 128 x 128 block, s = amax / 448 in binary32 (0 for an
+ * all-zero block) and each value goes to the e4m3 grid point nearest v / s
+ * (v / 1 when s == 0), ties to the even code.
+ * ------------------------------------------------------------------------- */
+
+/* |x| <= 448 (larger magnitudes are clamped) -> e4m3 FN byte, round to nearest even. */
+static uint8_t e4m3_nearest_even(float x) {
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    float a = fabsf(x);
+    if (a > 448.0f) a = 448.0f;
+    int ex;
+    frexpf(a, &ex);                        /* a = m * 2^ex, m in [0.5, 1) */
+    int binade = ex - 1;
+    if (binade < -6) binade = -6;          /* subnormals share the spacing of binade -6 */
+    const float quantum = ldexpf(1.0f, binade - 3);
+    const float r = rintf(a / quantum) * quantum;   /* exact division by a power of two; rintf ties to even */
+    if (r == 0.0f) return sign;
+    int ex2;
+    frexpf(r, &ex2);
+    const int e = ex2 - 1;
+    if (e < -6) return sign | (uint8_t)(r * 512.0f);              /* subnormal: r = m * 2^-9 */
+    const int m = (int)((ldexpf(r, -e) - 1.0f) * 8.0f);           /* exact */
+    return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/* E matrices of rows x K (rows and K multiples of 128), the same normals as
+ * syn_mxfp4_normal_batched, encoded as e4m3 codes [E][rows][K] and binary32
+ * block scales [E][rows/128][K/128]. */
+void syn_fp8block_normal_batched(uint64_t seed, uint64_t stream_base, int64_t E, int64_t rows, int64_t K,
+                                 float scale, uint8_t* codes, float* scales) {
+    const int64_t bands = rows / 128, KB = K / 128;
+    #pragma omp parallel
+    {
+        float* buf = (float*)malloc(sizeof(float) * 128 * (size_t)K);
+        #pragma omp for schedule(static) collapse(2)
+        for (int64_t e = 0; e < E; ++e) {
+            for (int64_t b = 0; b < bands; ++b) {
+                for (int64_t i = 0; i < 128; ++i)
+                    normal_range(seed, stream_base + (uint64_t)e, (b * 128 + i) * K, K, scale, buf + i * K);
+                for (int64_t c = 0; c < KB; ++c) {
+                    float amax = 0.0f;
+                    for (int64_t i = 0; i < 128; ++i)
+                        for (int64_t j = 0; j < 128; ++j) amax = fmaxf(amax, fabsf(buf[i * K + c * 128 + j]));
+                    const float s = amax / 448.0f;
+                    const float d = amax > 0.0f ? s : 1.0f;
+                    scales[(e * bands + b) * KB + c] = s;
+                    for (int64_t i = 0; i < 128; ++i) {
+                        uint8_t* row = codes + ((e * rows) + b * 128 + i) * K + c * 128;
+                        for (int64_t j = 0; j < 128; ++j) row[j] = e4m3_nearest_even(buf[i * K + c * 128 + j] / d);
+                    }
+                }
+            }
+        }
+        free(buf);
     }
 }
 

@@ -47,7 +47,7 @@ def weights(layer, packed=False):
         return W
     T, H = layer["x"].shape
     E, k = layer["w13"].shape[0], layer["top_k"]
-    p = moe.Problem.make(T, H, layer["w2"].shape[2] * 2, E, k)
+    p = moe.Problem.make(T, H, layer["w13"].shape[1] // 2, E, k)
     return moe.prepack_weights(p, W)
 
 
@@ -73,7 +73,7 @@ def problem(layer):
     import sparse_moe_expert_route_amd as moe
     T, H = layer["x"].shape
     E = layer["w13"].shape[0]
-    inter = layer["w2"].shape[2] * 2
+    inter = layer["w13"].shape[1] // 2
     return moe.Problem.make(T, H, inter, E, layer["top_k"], 1 if layer.get("score") == "sigmoid" else 0)
 
 

@@ -194,7 +194,7 @@ def _dense_bruteforce(layer):
         mask[t, ids[t]] = p / p.sum()
     xq, xs = F.quantize_fp8_blocks(F.decode_bf16(x))
     a = F.dequantize_fp8_blocks(xq, xs)
-    inter = layer["w2"].shape[2] * 2
+    inter = layer["w13"].shape[1] // 2
     y = np.zeros((T, H))
     for e in range(E):
         w13 = F.decode_mxfp4(layer["w13"][e], layer["w13_s"][e])
@@ -276,15 +276,15 @@ def _mutants():
     def silu_identity(z):
         return z
 
-    def gate_up_swapped(a, w13_e, w13_s_e, w2_e, w2_s_e):
+    def gate_up_swapped(a, w13_e, w13_s_e, w2_e, w2_s_e, fmt="mxfp4"):
         inter = w13_e.shape[0] // 2
         sw = np.concatenate([w13_e[inter:], w13_e[:inter]])
         sws = np.concatenate([w13_s_e[inter:], w13_s_e[:inter]])
-        return _orig_ffn(a, sw, sws, w2_e, w2_s_e)
+        return _orig_ffn(a, sw, sws, w2_e, w2_s_e, fmt)
 
-    def no_h_quant(a, w13_e, w13_s_e, w2_e, w2_s_e):
-        out = _orig_ffn(a, w13_e, w13_s_e, w2_e, w2_s_e)
-        out["y"] = out["h"] @ F.decode_mxfp4(w2_e, w2_s_e).T
+    def no_h_quant(a, w13_e, w13_s_e, w2_e, w2_s_e, fmt="mxfp4"):
+        out = _orig_ffn(a, w13_e, w13_s_e, w2_e, w2_s_e, fmt)
+        out["y"] = out["h"] @ OL.decode_expert_matrix(w2_e, w2_s_e, fmt).T
         return out
 
     def biased_softmax(logits, k, bias=None, score="softmax"):
