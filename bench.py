@@ -16,8 +16,10 @@ Prints ONE JSON line:
   graph_replay the same step captured once as a HIP graph and replayed
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 Workloads: tiny, flash_decode (default), flash_prefill, pro_decode,
-pro_skewed_prefill, their one-GPU tensor-parallel shares (*_tp4) and the
-speculative-verify blocks flash_verify, pro_verify (see synthetic/__init__.py).
+pro_skewed_prefill, their one-GPU tensor-parallel shares (*_tp4), the
+speculative-verify blocks flash_verify, pro_verify, and the FP8 block-scaled
+expert format (*_fp8: e4m3 weights, float32 128 x 128 block scales) (see
+synthetic/__init__.py).
 """
 
 import argparse
@@ -58,9 +60,11 @@ def parse():
 GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm.hip",
                 "sparse_moe_expert_route_amd/csrc/expert_gemm_tiled.hip",
                 "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
+FP8_GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm_fp8.hip",
+                    "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, sources):
     """HBM bytes per launch of the gate/up GEMM from the committed rocprofv3 counter summary
     (profiles/traffic_<workload>.md: FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None
     when there is none or the GEMM sources have changed since the counters were taken."""
@@ -75,7 +79,7 @@ def measured_traffic(workload):
         if len(parts) == 2 and parts[0] in ("gemm1_hbm_bytes_per_launch", "sources_sha256"):
             fields[parts[0]] = parts[1].strip()
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
+    for f in sources:
         h.update(open(os.path.join(here, f), "rb").read())
     if fields.get("sources_sha256") != h.hexdigest() or "gemm1_hbm_bytes_per_launch" not in fields:
         return None
@@ -96,6 +100,7 @@ def main():
 
     cfg = S.config(args.config)
     T, H, E, k, inter = cfg["T"], cfg["H"], cfg["E"], cfg["k"], cfg["I"]
+    fp8 = cfg["format"] == "fp8_block"
     N = T * k
     log("bench: workload %s T=%d H=%d E=%d k=%d I=%d" % (args.config, T, H, E, k, inter))
     t0 = time.time()
@@ -111,7 +116,7 @@ def main():
     x, wr = dev(lay["x"]), dev(lay["w_router"])
     bias = None if lay["bias"] is None else dev(lay["bias"])
     W = moe.ExpertWeights(dev(lay["w13"]), dev(lay["w13_s"]), dev(lay["w2"]), dev(lay["w2_s"]))
-    p = moe.Problem.make(T, H, inter, E, k)
+    p = moe.Problem.make(T, H, inter, E, k, 0, moe.EXPERTS_FP8_BLOCK if fp8 else moe.EXPERTS_MXFP4)
     prepack_ms = None
     if not args.canonical_weights:
         # one-time reordering of the expert code bytes at load time (untimed; reported)
@@ -180,9 +185,9 @@ def main():
     st = torch.empty(N, dtype=torch.int32, device="cuda")
     ros = torch.empty(N, dtype=torch.int32, device="cuda")
     xq = torch.empty(N, H, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(N, H // 128, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(N, H // 128, dtype=moe.scale_dtype(p), device="cuda")
     hq = torch.empty(N, inter, dtype=torch.uint8, device="cuda")
-    hs = torch.empty(N, inter // 128, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(N, inter // 128, dtype=moe.scale_dtype(p), device="cuda")
     moe.route(p, x, wr, bias, logits, ids, w)
     moe.permute(p, ids, x, off, st, ros, xq, xs, ws)
     torch.cuda.synchronize()
@@ -199,8 +204,13 @@ def main():
     torch.cuda.synchronize()
     gemm1_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
 
-    w13_bytes_per_expert = 2 * inter * (H // 2 + H // 32)
-    gemm1_bytes = touched * w13_bytes_per_expert + N * (H + H // 128) + N * (inter + inter // 128)
+    if fp8:
+        # e4m3 codes + one float32 per 128 x 128 block; activation and h scales float32
+        w13_bytes_per_expert = 2 * inter * H + (2 * inter // 128) * (H // 128) * 4
+        gemm1_bytes = touched * w13_bytes_per_expert + N * (H + 4 * H // 128) + N * (inter + 4 * inter // 128)
+    else:
+        w13_bytes_per_expert = 2 * inter * (H // 2 + H // 32)
+        gemm1_bytes = touched * w13_bytes_per_expert + N * (H + H // 128) + N * (inter + inter // 128)
     gemm1_flops = 2.0 * N * 2 * inter * H
     # the kernel's bound: below the ridge point (peak FLOP/s over peak bytes/s, 625 FLOP/byte)
     # the weight and activation bytes take longer than the MFMA work
@@ -213,16 +223,18 @@ def main():
         achieved = gemm1_flops / (gemm1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
-    roof["traffic"] = measured_traffic(args.config) if not args.canonical_weights else None
-    tiled = N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= 6144
-    roof["kernel"] = ("expert_gemm_tiled_kernel" if tiled else "expert_gemm_stream_kernel") + \
+    roof["traffic"] = None if args.canonical_weights else \
+        measured_traffic(args.config, FP8_GEMM_SOURCES if fp8 else GEMM_SOURCES)
+    tiled = not fp8 and N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= 6144
+    roof["kernel"] = ("expert_gemm_fp8_stream_kernel" if fp8 else
+                      "expert_gemm_tiled_kernel" if tiled else "expert_gemm_stream_kernel") + \
         "<gate/up + SwiGLU + FP8 requant>"
     roof["launch_ms"] = round(gemm1_ms, 4)
     roof["algorithmic_bytes"] = int(gemm1_bytes)
     roof["algorithmic_flops"] = gemm1_flops
 
     # whole-layer work per step (touched experts' weights + router + x + y; FLOPs of both expert GEMMs)
-    expert_bytes = 3 * H * inter * 17 // 32
+    expert_bytes = 3 * H * inter + 3 * (H // 128) * (inter // 128) * 4 if fp8 else 3 * H * inter * 17 // 32
     layer_bytes = touched * expert_bytes + E * H * 2 + T * H * 2 + T * H * 4
     layer_flops = 2.0 * N * 3 * inter * H
     step_s = ms_per_step * 1e-3
@@ -233,10 +245,12 @@ def main():
 
     out = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3 x mxfp4 (fp32 acc)",
-           "data": "synthetic (seeded; N(0,1) bf16 activations, 0.02*N(0,1) bf16 router and MXFP4 experts)",
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "fp8e4m3 x fp8e4m3 block-scaled (fp32 acc)" if fp8 else "fp8e4m3 x mxfp4 (fp32 acc)",
+           "data": "synthetic (seeded; N(0,1) bf16 activations, 0.02*N(0,1) bf16 router and %s experts)"
+                   % ("FP8 block-scaled" if fp8 else "MXFP4"),
            "config": {"workload": args.config, "T": T, "H": H, "E": E, "k": k, "I": inter, "seed": args.seed,
-                      "bias": cfg["bias"]},
+                      "bias": cfg["bias"], "experts": cfg["format"]},
            "roofline": roof, "layer": layer,
            "graph_replay": graph,
            "weight_layout": "canonical" if args.canonical_weights else "packed",
@@ -269,7 +283,8 @@ def cpu_baseline(lay, args, T):
     sec = time.perf_counter() - t0
     return {"value": round(n / sec, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": "first %d tokens of the %s workload, whole layer (router, routing, FP8 quantisation, all "
-                      "their experts decoded from MXFP4 and run in float64, combine); %.1f s" % (n, args.config, sec)}
+                      "their experts decoded from %s and run in float64, combine); %.1f s"
+                      % (n, args.config, "FP8 blocks" if lay.get("format") == "fp8_block" else "MXFP4", sec)}
 
 
 if __name__ == "__main__":

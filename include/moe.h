@@ -47,7 +47,7 @@ extern "C" {
 /* Same declaration as the HIP runtime's: a stream handle is an opaque pointer. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
     MOE_OK = 0,
@@ -69,6 +69,18 @@ typedef enum { MOE_SCORE_SOFTMAX_TOPK = 0, MOE_SCORE_SIGMOID_BIAS = 1 } moe_scor
 
 typedef enum { MOE_OUT_F32 = 0, MOE_OUT_BF16 = 1 } moe_out_dtype;
 
+/* Storage format of the expert weights, and with it the activation scales.
+ * MOE_EXPERTS_MXFP4: the V2.6 experts (teardown, "Why Are the V2.6 Files
+ *   Half the Size of V2.5?", table row "Routed experts"): see
+ *   moe_expert_weights.  Activation and h scales are e8m0 bytes (powers of
+ *   two), one per row per 128 channels.
+ * MOE_EXPERTS_FP8_BLOCK: the V2.5 experts of the same table: e4m3 codes with
+ *   one float32 scale per 128 x 128 block.  Activation and h scales are
+ *   float32, one per row per 128 channels: scale = amax / 448 and codes =
+ *   round-to-nearest-even e4m3 of v / scale, both binary32 divisions (an
+ *   all-zero run stores scale 0 and the codes of v / 1).                   */
+typedef enum { MOE_EXPERTS_MXFP4 = 0, MOE_EXPERTS_FP8_BLOCK = 1 } moe_expert_format;
+
 typedef struct {
     int64_t num_tokens;    /* T  */
     int32_t hidden;        /* H  (multiple of 128) */
@@ -76,16 +88,23 @@ typedef struct {
     int32_t num_experts;   /* E  */
     int32_t top_k;         /* k  */
     int32_t score_func;    /* moe_score_func */
+    int32_t expert_format; /* moe_expert_format */
 } moe_problem;
 
-/* MXFP4 expert weights ("two 4-bit values per byte (U8), one 8-bit scale per
- * 32 values": teardown, "Why Are the V2.6 Files Half the Size of V2.5?").
+/* MXFP4 expert weights (teardown, "Why Are the V2.6 Files Half the Size of
+ * V2.5?", table row "Routed experts": a byte holds two e2m1 values, and each
+ * run of 32 values shares one e8m0 scale).
  * Element 2i of a row is in bits 3:0 of byte i, element 2i+1 in bits 7:4.
  * Scales are e8m0 bytes (2^(b-127)), one per 32 consecutive elements of a row.
  *   w13       [E][2I][H/2]   rows 0..I-1 gate, rows I..2I-1 up
  *   w13_scale [E][2I][H/32]
  *   w2        [E][H][I/2]
- *   w2_scale  [E][H][I/32]                                                */
+ *   w2_scale  [E][H][I/32]
+ * FP8 block-scaled experts (problem->expert_format == MOE_EXPERTS_FP8_BLOCK):
+ *   w13       [E][2I][H]        e4m3 codes, rows 0..I-1 gate, I..2I-1 up
+ *   w13_scale [E][2I/128][H/128] float32, one per 128 x 128 block
+ *   w2        [E][H][I]         e4m3 codes
+ *   w2_scale  [E][H/128][I/128] float32                                   */
 /* Layout of the code and scale bytes (w13, w13_scale, w2, w2_scale).
  * MOE_WEIGHTS_CANONICAL: row-major as above (the checkpoint's layout).
  * MOE_WEIGHTS_PACKED: the layout moe_prepack_weights writes.  For one
@@ -99,6 +118,10 @@ typedef struct {
  *   Scales (K/32 bytes per row): group q, step c is a 64-byte block at byte
  *   offset (q * K/128 + c) * 64 of the expert's scale matrix; in it, the 4
  *   scale bytes of row 16q + r for columns [128c, 128c + 128) sit at 4r.
+ *   FP8 block-scaled experts (K bytes per row): group q, step c is a
+ *   2048-byte block at byte offset (q * K/128 + c) * 2048; in it, bytes
+ *   [128c + 16p, 128c + 16p + 16) of row 16q + r (p = 0..7) sit at
+ *   (16p + r) * 16.  Their float32 scales keep the canonical layout.
  *   Same bytes, reordered so that one 64-lane load covers whole cache lines. */
 typedef enum { MOE_WEIGHTS_CANONICAL = 0, MOE_WEIGHTS_PACKED = 1 } moe_weight_layout;
 
@@ -125,6 +148,8 @@ size_t moe_workspace_size(const moe_problem* problem);
  *   weights           canonical layout (layout == MOE_WEIGHTS_CANONICAL)
  *   w13_packed        [E][2I][H/2] bytes out, w13_scale_packed [E][2I][H/32],
  *   w2_packed         [E][H][I/2] bytes out,  w2_scale_packed  [E][H][I/32];
+ *                     (FP8 block-scaled experts: the sizes of w13, w13_scale,
+ *                     w2 and w2_scale in that format; scales are copied);
  *                     16-byte aligned, none overlapping another or an input
  * The packed weights are then passed as {w13_packed, w13_scale_packed,
  * w2_packed, w2_scale_packed, MOE_WEIGHTS_PACKED}.                         */
@@ -156,13 +181,15 @@ moe_status moe_route(const moe_problem* problem, const void* x_bf16, const void*
  *   sorted_token   [T*k]        int32 out: token of each expert-ordered row
  *   row_of_slot    [T*k]        int32 out: expert-ordered row of each slot
  *   xq_perm        [T*k][H]     e4m3 out: FP8 codes of x[sorted_token[r]]
- *   xs_perm        [T*k][H/128] e8m0 out: per-128-channel power-of-two scale
- * The FP8 rule: amax of each 128-channel run, scale 2^e with e the smallest
- * integer such that amax / 2^e <= 448, codes = round-to-nearest-even e4m3 of
- * x / 2^e (an all-zero run gets scale byte 0).                            */
+ *   xs_perm        [T*k][H/128] out: per-128-channel scale, e8m0 bytes
+ *                               (MXFP4 experts) or float32 (FP8 block-scaled)
+ * The FP8 rule for MXFP4 experts: amax of each 128-channel run, scale 2^e
+ * with e the smallest integer such that amax / 2^e <= 448, codes =
+ * round-to-nearest-even e4m3 of x / 2^e (an all-zero run gets scale byte 0).
+ * For FP8 block-scaled experts: the float32 rule of moe_expert_format.     */
 moe_status moe_permute(const moe_problem* problem, const int32_t* topk_ids, const void* x_bf16,
                        int32_t* expert_offsets, int32_t* sorted_token, int32_t* row_of_slot,
-                       uint8_t* xq_perm, uint8_t* xs_perm, void* workspace, size_t workspace_bytes,
+                       uint8_t* xq_perm, void* xs_perm, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
 /* The experts on their rows: gate/up projection, SwiGLU, FP8 requantisation
@@ -172,30 +199,31 @@ moe_status moe_permute(const moe_problem* problem, const int32_t* topk_ids, cons
  *   xq_perm, xs_perm, expert_offsets  as produced by moe_permute
  *   y_perm [T*k][H] fp32 out: expert output of each row (unweighted)       */
 moe_status moe_grouped_gemm_swiglu(const moe_problem* problem, const uint8_t* xq_perm,
-                                   const uint8_t* xs_perm, const int32_t* expert_offsets,
+                                   const void* xs_perm, const int32_t* expert_offsets,
                                    const moe_expert_weights* weights, float* y_perm,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* First half of moe_grouped_gemm_swiglu: gate/up projection, SwiGLU
  * h = silu(g) * u with silu(z) = z / (1 + e^-z), and FP8 quantisation of h
  * with the rule of moe_permute.
- *   hq_perm [T*k][I] e4m3 out, hs_perm [T*k][I/128] e8m0 out              */
+ *   hq_perm [T*k][I] e4m3 out, hs_perm [T*k][I/128] out (e8m0 bytes, or
+ *   float32 for FP8 block-scaled experts)                                 */
 moe_status moe_grouped_gemm1_swiglu(const moe_problem* problem, const uint8_t* xq_perm,
-                                    const uint8_t* xs_perm, const int32_t* expert_offsets,
+                                    const void* xs_perm, const int32_t* expert_offsets,
                                     const moe_expert_weights* weights, uint8_t* hq_perm,
-                                    uint8_t* hs_perm, void* workspace, size_t workspace_bytes,
+                                    void* hs_perm, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
 /* Gate/up pre-activations only (for exactness checks of the block-scaled
  * product): gu_perm [T*k][2I] fp32 out, columns 0..I-1 gate, I..2I-1 up.  */
 moe_status moe_grouped_gemm1_preact(const moe_problem* problem, const uint8_t* xq_perm,
-                                    const uint8_t* xs_perm, const int32_t* expert_offsets,
+                                    const void* xs_perm, const int32_t* expert_offsets,
                                     const moe_expert_weights* weights, float* gu_perm,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Second half of moe_grouped_gemm_swiglu: y_perm = h . W2_e^T per row.     */
 moe_status moe_grouped_gemm2(const moe_problem* problem, const uint8_t* hq_perm,
-                             const uint8_t* hs_perm, const int32_t* expert_offsets,
+                             const void* hs_perm, const int32_t* expert_offsets,
                              const moe_expert_weights* weights, float* y_perm,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -20,7 +20,8 @@ __all__ = [
     "MoeError", "Problem", "ExpertWeights", "lib_path", "load", "abi_version", "workspace_size",
     "alloc_workspace", "prepack_weights", "route", "permute", "grouped_gemm_swiglu", "grouped_gemm1_swiglu",
     "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "OUT_F32", "OUT_BF16",
-    "WEIGHTS_CANONICAL", "WEIGHTS_PACKED", "EXPORTED_SYMBOLS",
+    "WEIGHTS_CANONICAL", "WEIGHTS_PACKED", "EXPERTS_MXFP4", "EXPERTS_FP8_BLOCK", "EXPORTED_SYMBOLS",
+    "scale_dtype",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,8 @@ OUT_F32 = 0
 OUT_BF16 = 1
 WEIGHTS_CANONICAL = 0
 WEIGHTS_PACKED = 1
+EXPERTS_MXFP4 = 0
+EXPERTS_FP8_BLOCK = 1
 
 EXPORTED_SYMBOLS = [
     "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_prepack_weights", "moe_route", "moe_permute",
@@ -47,11 +50,11 @@ class MoeError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int32),
                 ("intermediate", ctypes.c_int32), ("num_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("score_func", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("score_func", ctypes.c_int32), ("expert_format", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, T, H, I, E, k, score_func=0):
-        return cls(int(T), int(H), int(I), int(E), int(k), int(score_func))
+    def make(cls, T, H, I, E, k, score_func=0, expert_format=EXPERTS_MXFP4):
+        return cls(int(T), int(H), int(I), int(E), int(k), int(score_func), int(expert_format))
 
     @property
     def N(self):
@@ -63,22 +66,37 @@ class _Weights(ctypes.Structure):
                 ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
+def _weight_specs(p):
+    """(dtype, shape) of w13, w13_scale, w2, w2_scale for the problem's expert format."""
+    E, H, I = p.num_experts, p.hidden, p.intermediate
+    if p.expert_format == EXPERTS_FP8_BLOCK:
+        return [(torch.uint8, (E, 2 * I, H)), (torch.float32, (E, 2 * I // 128, H // 128)),
+                (torch.uint8, (E, H, I)), (torch.float32, (E, H // 128, I // 128))]
+    return [(torch.uint8, (E, 2 * I, H // 2)), (torch.uint8, (E, 2 * I, H // 32)),
+            (torch.uint8, (E, H, I // 2)), (torch.uint8, (E, H, I // 32))]
+
+
+def scale_dtype(p):
+    """dtype of the activation and h scales: uint8 (e8m0) or float32 (FP8 block-scaled experts)."""
+    return torch.float32 if p.expert_format == EXPERTS_FP8_BLOCK else torch.uint8
+
+
 class ExpertWeights:
-    """Device tensors of the MXFP4 experts (uint8):
-    w13 [E, 2I, H/2], w13_scale [E, 2I, H/32], w2 [E, H, I/2], w2_scale [E, H, I/32].
-    ``layout`` says how the code bytes of w13 and w2 are ordered: WEIGHTS_CANONICAL
-    (row-major) or WEIGHTS_PACKED (as written by ``prepack_weights``; same shapes)."""
+    """Device tensors of the experts.  MXFP4 (uint8): w13 [E, 2I, H/2], w13_scale
+    [E, 2I, H/32], w2 [E, H, I/2], w2_scale [E, H, I/32].  FP8 block-scaled: w13 [E, 2I, H]
+    uint8, w13_scale [E, 2I/128, H/128] float32, w2 [E, H, I] uint8, w2_scale
+    [E, H/128, I/128] float32.  ``layout`` says how the code bytes are ordered:
+    WEIGHTS_CANONICAL (row-major) or WEIGHTS_PACKED (as written by ``prepack_weights``;
+    same shapes)."""
 
     def __init__(self, w13, w13_scale, w2, w2_scale, layout=WEIGHTS_CANONICAL):
         self.w13, self.w13_scale, self.w2, self.w2_scale = w13, w13_scale, w2, w2_scale
         self.layout = int(layout)
 
     def check(self, p):
-        E, H, I = p.num_experts, p.hidden, p.intermediate
-        _check(self.w13, torch.uint8, (E, 2 * I, H // 2), "w13")
-        _check(self.w13_scale, torch.uint8, (E, 2 * I, H // 32), "w13_scale")
-        _check(self.w2, torch.uint8, (E, H, I // 2), "w2")
-        _check(self.w2_scale, torch.uint8, (E, H, I // 32), "w2_scale")
+        for t, (dt, shape), name in zip((self.w13, self.w13_scale, self.w2, self.w2_scale), _weight_specs(p),
+                                        ("w13", "w13_scale", "w2", "w2_scale")):
+            _check(t, dt, shape, name)
 
     def struct(self):
         return _Weights(self.w13.data_ptr(), self.w13_scale.data_ptr(),
@@ -174,7 +192,7 @@ def prepack_weights(p, weights, w13_packed=None, w2_packed=None, w13_scale_packe
     for given, src, name in ((w13_packed, weights.w13, "w13_packed"), (w13_scale_packed, weights.w13_scale, "w13_scale_packed"),
                              (w2_packed, weights.w2, "w2_packed"), (w2_scale_packed, weights.w2_scale, "w2_scale_packed")):
         t = torch.empty_like(src) if given is None else given
-        _check(t, torch.uint8, tuple(src.shape), name)
+        _check(t, src.dtype, tuple(src.shape), name)
         outs.append(t)
     W = weights.struct()
     st = load().moe_prepack_weights(ctypes.byref(p), ctypes.byref(W), _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]),
@@ -210,7 +228,7 @@ def permute(p, topk_ids, x, expert_offsets, sorted_token, row_of_slot, xq_perm, 
     _check(sorted_token, torch.int32, (N,), "sorted_token")
     _check(row_of_slot, torch.int32, (N,), "row_of_slot")
     _check(xq_perm, torch.uint8, (N, H), "xq_perm")
-    _check(xs_perm, torch.uint8, (N, H // 128), "xs_perm")
+    _check(xs_perm, scale_dtype(p), (N, H // 128), "xs_perm")
     st = load().moe_permute(ctypes.byref(p), _ptr(topk_ids), _ptr(x), _ptr(expert_offsets), _ptr(sorted_token),
                             _ptr(row_of_slot), _ptr(xq_perm), _ptr(xs_perm), _ptr(ws), ws.numel(),
                             _stream(stream))
@@ -220,7 +238,7 @@ def permute(p, topk_ids, x, expert_offsets, sorted_token, row_of_slot, xq_perm, 
 def _gemm_inputs(p, act, act_scale, K, expert_offsets, weights):
     N = p.N
     _check(act, torch.uint8, (N, K), "activations")
-    _check(act_scale, torch.uint8, (N, K // 128), "activation scales")
+    _check(act_scale, scale_dtype(p), (N, K // 128), "activation scales")
     _check(expert_offsets, torch.int32, (p.num_experts + 1,), "expert_offsets")
     weights.check(p)
 
@@ -237,7 +255,7 @@ def grouped_gemm_swiglu(p, xq_perm, xs_perm, expert_offsets, weights, y_perm, ws
 def grouped_gemm1_swiglu(p, xq_perm, xs_perm, expert_offsets, weights, hq_perm, hs_perm, ws, stream=None):
     _gemm_inputs(p, xq_perm, xs_perm, p.hidden, expert_offsets, weights)
     _check(hq_perm, torch.uint8, (p.N, p.intermediate), "hq_perm")
-    _check(hs_perm, torch.uint8, (p.N, p.intermediate // 128), "hs_perm")
+    _check(hs_perm, scale_dtype(p), (p.N, p.intermediate // 128), "hs_perm")
     w = weights.struct()
     st = load().moe_grouped_gemm1_swiglu(ctypes.byref(p), _ptr(xq_perm), _ptr(xs_perm), _ptr(expert_offsets),
                                          ctypes.byref(w), _ptr(hq_perm), _ptr(hs_perm), _ptr(ws), ws.numel(),

@@ -31,9 +31,14 @@ moe_status check_problem(const moe_problem* p) {
     if (p->num_experts < 1 || p->num_experts > 512) return MOE_ERR_INVALID_ARGUMENT;
     if (p->top_k < 1 || p->top_k > 8 || p->top_k > p->num_experts) return MOE_ERR_INVALID_ARGUMENT;
     if (p->score_func != MOE_SCORE_SOFTMAX_TOPK && p->score_func != MOE_SCORE_SIGMOID_BIAS) return MOE_ERR_UNSUPPORTED;
+    if (p->expert_format != MOE_EXPERTS_MXFP4 && p->expert_format != MOE_EXPERTS_FP8_BLOCK) return MOE_ERR_UNSUPPORTED;
     if (p->num_tokens * (int64_t)p->top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
+
+bool fp8_block(const moe_problem& p) { return p.expert_format == MOE_EXPERTS_FP8_BLOCK; }
+// bytes of one activation / h scale: e8m0, or float32 with FP8 block-scaled experts
+size_t scale_bytes(const moe_problem& p) { return fp8_block(p) ? 4 : 1; }
 
 Layout layout_of(const moe_problem& p) {
     const size_t T = (size_t)p.num_tokens, k = (size_t)p.top_k, N = T * k;
@@ -52,10 +57,11 @@ Layout layout_of(const moe_problem& p) {
     L.block_base = take(nblk * E * 4);
     L.tile_start = take((E + 1) * 4);
     L.tile_info = take((size_t)max_tiles((int64_t)N, (int)E, kRowsPerTile) * 16);   // bound for both tile sizes
+    const size_t sb = scale_bytes(p);
     L.xq = take(N * H);
-    L.xs = take(N * (H / kFp8Block));
+    L.xs = take(N * (H / kFp8Block) * sb);
     L.hq = take(N * I);
-    L.hs = take(N * (I / kFp8Block));
+    L.hs = take(N * (I / kFp8Block) * sb);
     L.y_perm = take(N * H * 4);
     L.total = off;
     return L;
@@ -115,7 +121,7 @@ bool use_tiled(const moe_problem& p);
 // does the whole permutation and also writes the GEMMs' tile plan into the
 // workspace; *planned tells the caller that it may skip the plan.
 moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, int32_t* offsets,
-                       int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, uint8_t* xs, void* ws,
+                       int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, void* xs, void* ws,
                        hipStream_t stream, bool* planned = nullptr, bool fuse_gather = false) {
     const Layout L = layout_of(p);
     const int64_t N = p.num_tokens * p.top_k;
@@ -137,19 +143,20 @@ moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, 
     // fused gather: quantise the T tokens once; GEMM-1 reads them through sorted_token
     if (fuse_gather)
         MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, nullptr, xq, xs, p.num_tokens, p.hidden, p.num_tokens,
-                                       stream));
+                                       fp8_block(p), stream));
     else
-        MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens, stream));
+        MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens,
+                                       fp8_block(p), stream));
     return MOE_OK;
 }
 
-GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_scale, const int32_t* offsets,
+GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const void* act_scale, const int32_t* offsets,
                    const int32_t* tile_start, const int4* tile_info, const uint8_t* w, const uint8_t* w_scale, void* out,
-                   uint8_t* out_scale) {
+                   void* out_scale) {
     GemmArgs a;
-    a.act = act; a.act_scale = act_scale; a.offsets = offsets; a.tile_start = tile_start; a.tile_info = tile_info;
+    a.act = act; a.act_scale = (const uint8_t*)act_scale; a.offsets = offsets; a.tile_start = tile_start; a.tile_info = tile_info;
     a.act_rows = nullptr;
-    a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = out_scale;
+    a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = (uint8_t*)out_scale;
     a.packed = 0;
     a.N = p.num_tokens * p.top_k;
     a.H = p.hidden; a.I = p.intermediate; a.E = p.num_experts;
@@ -161,20 +168,22 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const uint8_t* act_
 // depends on host-known sizes only, so both GEMMs of one call agree on it.
 // The tiled kernel addresses activations with 32-bit offsets: every
 // activation matrix it reads ([T*k][H] or [T][H], [T*k][I]) stays under 2 GiB.
+// FP8 block-scaled experts always take their own streaming kernel.
 bool use_tiled(const moe_problem& p) {
     const int64_t rows = p.num_tokens * p.top_k;
     const int64_t widest = p.hidden > p.intermediate ? p.hidden : p.intermediate;
-    return tiled_gemm_supported(p.hidden, p.intermediate) && rows >= 32 * (int64_t)p.num_experts &&
+    return !fp8_block(p) && tiled_gemm_supported(p.hidden, p.intermediate) && rows >= 32 * (int64_t)p.num_experts &&
            rows * widest < ((int64_t)1 << 31);
 }
 
 moe_status launch_gemm(const moe_problem& p, GemmMode mode, const GemmArgs& a, hipStream_t stream) {
-    MOE_LAUNCH(use_tiled(p) ? launch_expert_gemm_tiled(mode, a, stream) : launch_expert_gemm(mode, a, stream));
+    if (fp8_block(p)) MOE_LAUNCH(launch_expert_gemm_fp8(mode, a, stream));
+    else MOE_LAUNCH(use_tiled(p) ? launch_expert_gemm_tiled(mode, a, stream) : launch_expert_gemm(mode, a, stream));
     return MOE_OK;
 }
 
-moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, const uint8_t* xs,
-                     const int32_t* offsets, const moe_expert_weights& wt, void* out, uint8_t* out_scale,
+moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, const void* xs,
+                     const int32_t* offsets, const moe_expert_weights& wt, void* out, void* out_scale,
                      void* ws, bool plan, hipStream_t stream, const int32_t* act_rows = nullptr) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
@@ -189,7 +198,7 @@ moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, con
     return launch_gemm(p, mode, a, stream);
 }
 
-moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const uint8_t* hs, const int32_t* offsets,
+moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const void* hs, const int32_t* offsets,
                      const moe_expert_weights& wt, float* y_perm, void* ws, bool plan, hipStream_t stream) {
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
@@ -233,14 +242,27 @@ moe_status moe_prepack_weights(const moe_problem* p, const moe_expert_weights* w
     if (weights->layout != MOE_WEIGHTS_CANONICAL) return MOE_ERR_INVALID_ARGUMENT;
     if (!all_aligned(w13_packed, w13_scale_packed, w2_packed, w2_scale_packed)) return MOE_ERR_INVALID_ARGUMENT;
     const size_t E = (size_t)p->num_experts, H = (size_t)p->hidden, I = (size_t)p->intermediate;
+    const bool f8 = fp8_block(*p);
     const uint8_t* in[4] = {weights->w13, weights->w13_scale, weights->w2, weights->w2_scale};
     const uint8_t* out[4] = {w13_packed, w13_scale_packed, w2_packed, w2_scale_packed};
-    const size_t n[4] = {E * 2 * I * (H / 2), E * 2 * I * (H / 32), E * H * (I / 2), E * H * (I / 32)};
+    const size_t n[4] = {f8 ? E * 2 * I * H : E * 2 * I * (H / 2),
+                         f8 ? E * (2 * I / 128) * (H / 128) * 4 : E * 2 * I * (H / 32),
+                         f8 ? E * H * I : E * H * (I / 2),
+                         f8 ? E * (H / 128) * (I / 128) * 4 : E * H * (I / 32)};
     for (int i = 0; i < 4; ++i) {
         for (int j = 0; j < 4; ++j) {
             if (overlaps(out[i], n[i], in[j], n[j])) return MOE_ERR_INVALID_ARGUMENT;
             if (j != i && overlaps(out[i], n[i], out[j], n[j])) return MOE_ERR_INVALID_ARGUMENT;
         }
+    }
+    if (f8) {
+        // e4m3 rows of K bytes are packed like e2m1 rows of 2K columns; the
+        // float32 block scales keep their layout
+        MOE_LAUNCH(launch_prepack(weights->w13, w13_packed, (int64_t)(E * 2 * I), (int)(2 * H), stream));
+        MOE_LAUNCH(launch_prepack(weights->w2, w2_packed, (int64_t)(E * H), (int)(2 * I), stream));
+        MOE_LAUNCH(hipMemcpyAsync(w13_scale_packed, weights->w13_scale, n[1], hipMemcpyDeviceToDevice, stream));
+        MOE_LAUNCH(hipMemcpyAsync(w2_scale_packed, weights->w2_scale, n[3], hipMemcpyDeviceToDevice, stream));
+        return MOE_OK;
     }
     MOE_LAUNCH(launch_prepack(weights->w13, w13_packed, (int64_t)(E * 2 * I), (int)H, stream));
     MOE_LAUNCH(launch_prepack_scales(weights->w13_scale, w13_scale_packed, (int64_t)(E * 2 * I), (int)H, stream));
@@ -261,7 +283,7 @@ moe_status moe_route(const moe_problem* p, const void* x_bf16, const void* w_rou
 }
 
 moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, const void* x_bf16, int32_t* expert_offsets,
-                       int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq_perm, uint8_t* xs_perm,
+                       int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq_perm, void* xs_perm,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK(check_problem(p));
     if (!all_aligned(topk_ids, x_bf16, expert_offsets, sorted_token, row_of_slot, xq_perm, xs_perm))
@@ -271,9 +293,9 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, const void
     return run_permute(*p, topk_ids, x_bf16, expert_offsets, sorted_token, row_of_slot, xq_perm, xs_perm, ws, stream);
 }
 
-moe_status moe_grouped_gemm1_swiglu(const moe_problem* p, const uint8_t* xq_perm, const uint8_t* xs_perm,
+moe_status moe_grouped_gemm1_swiglu(const moe_problem* p, const uint8_t* xq_perm, const void* xs_perm,
                                     const int32_t* expert_offsets, const moe_expert_weights* weights,
-                                    uint8_t* hq_perm, uint8_t* hs_perm, void* ws, size_t ws_bytes,
+                                    uint8_t* hq_perm, void* hs_perm, void* ws, size_t ws_bytes,
                                     hipStream_t stream) {
     MOE_CHECK(check_problem(p));
     MOE_CHECK(check_weights(weights));
@@ -284,7 +306,7 @@ moe_status moe_grouped_gemm1_swiglu(const moe_problem* p, const uint8_t* xq_perm
                      stream);
 }
 
-moe_status moe_grouped_gemm1_preact(const moe_problem* p, const uint8_t* xq_perm, const uint8_t* xs_perm,
+moe_status moe_grouped_gemm1_preact(const moe_problem* p, const uint8_t* xq_perm, const void* xs_perm,
                                     const int32_t* expert_offsets, const moe_expert_weights* weights,
                                     float* gu_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK(check_problem(p));
@@ -296,7 +318,7 @@ moe_status moe_grouped_gemm1_preact(const moe_problem* p, const uint8_t* xq_perm
                      stream);
 }
 
-moe_status moe_grouped_gemm2(const moe_problem* p, const uint8_t* hq_perm, const uint8_t* hs_perm,
+moe_status moe_grouped_gemm2(const moe_problem* p, const uint8_t* hq_perm, const void* hs_perm,
                              const int32_t* expert_offsets, const moe_expert_weights* weights, float* y_perm,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK(check_problem(p));
@@ -307,7 +329,7 @@ moe_status moe_grouped_gemm2(const moe_problem* p, const uint8_t* hq_perm, const
     return run_gemm2(*p, hq_perm, hs_perm, expert_offsets, *weights, y_perm, ws, true, stream);
 }
 
-moe_status moe_grouped_gemm_swiglu(const moe_problem* p, const uint8_t* xq_perm, const uint8_t* xs_perm,
+moe_status moe_grouped_gemm_swiglu(const moe_problem* p, const uint8_t* xq_perm, const void* xs_perm,
                                    const int32_t* expert_offsets, const moe_expert_weights* weights, float* y_perm,
                                    void* ws, size_t ws_bytes, hipStream_t stream) {
     MOE_CHECK(check_problem(p));
@@ -317,7 +339,7 @@ moe_status moe_grouped_gemm_swiglu(const moe_problem* p, const uint8_t* xq_perm,
     if (p->num_tokens == 0) return MOE_OK;
     const Layout L = layout_of(*p);
     uint8_t* hq = at<uint8_t>(ws, L.hq);
-    uint8_t* hs = at<uint8_t>(ws, L.hs);
+    void* hs = at<uint8_t>(ws, L.hs);
     MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq_perm, xs_perm, expert_offsets, *weights, hq, hs, ws, true, stream));
     return run_gemm2(*p, hq, hs, expert_offsets, *weights, y_perm, ws, false, stream);
 }
@@ -351,9 +373,9 @@ moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_r
     int32_t* st = at<int32_t>(ws, L.sorted_token);
     int32_t* ros = at<int32_t>(ws, L.row_of_slot);
     uint8_t* xq = at<uint8_t>(ws, L.xq);
-    uint8_t* xs = at<uint8_t>(ws, L.xs);
+    void* xs = at<uint8_t>(ws, L.xs);
     uint8_t* hq = at<uint8_t>(ws, L.hq);
-    uint8_t* hs = at<uint8_t>(ws, L.hs);
+    void* hs = at<uint8_t>(ws, L.hs);
     float* y_perm = at<float>(ws, L.y_perm);
     MOE_CHECK(run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, ids, w, stream));
     // the FP8 gather is fused into GEMM-1: x is quantised once per token (T rows

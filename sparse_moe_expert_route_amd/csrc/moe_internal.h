@@ -31,6 +31,16 @@ __device__ __forceinline__ int fp8_block_exponent(float amax) {
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
+// FP8 quantisation with a float32 scale (FP8 block-scaled experts): the
+// scale of a 128-channel block is amax / 448 and each code is the e4m3
+// rounding of v / scale, both IEEE binary32 divisions (hipcc's default fp32
+// division is correctly rounded).  The quotient can exceed 448 by one
+// rounding; such values round to 448 anyway, and the clamp keeps the
+// conversion away from its saturation path.  An all-zero block stores scale
+// 0 and divides by 1.
+__device__ __forceinline__ float fp8_f32_scale(float amax) { return amax / 448.0f; }
+__device__ __forceinline__ float fp8_f32_quotient(float v, float d) { return fminf(fmaxf(v / d, -448.0f), 448.0f); }
+
 // Four floats (already divided by their block scale, |v| <= 448) -> four
 // e4m3 bytes, round to nearest even (v_cvt_pk_fp8_f32), byte i = v[i].
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
@@ -77,8 +87,9 @@ hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, co
 hipError_t launch_perm_small(const int32_t* ids, int32_t* offsets, int32_t* sorted_token, int32_t* row_of_slot,
                              int32_t* tile_start, int4* tile_info, int64_t N, int E, int k, int rows_per_tile,
                              int max_tiles, hipStream_t stream);
+// xs: e8m0 bytes (power-of-two scales), or float32 when f32_scales is set
 hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq,
-                               uint8_t* xs, int64_t N, int H, int64_t T, hipStream_t stream);
+                               void* xs, int64_t N, int H, int64_t T, int f32_scales, hipStream_t stream);
 
 // Byte permutation of a matrix of `rows` rows x K e2m1 columns (K/2 bytes per
 // row, rows a multiple of 16, K a multiple of 128) into the packed weight
@@ -96,19 +107,20 @@ enum GemmMode { kGemm1Swiglu = 0, kGemm1Preact = 1, kGemm2 = 2 };
 
 // Grouped expert GEMM over the expert-ordered rows.  For gemm1 modes the
 // weights are W13 [E][2I][H/2] and K = H; for gemm2 they are W2 [E][H][I/2]
-// and K = I.
+// and K = I.  FP8 block-scaled experts: codes [E][2I][H] / [E][H][I] e4m3,
+// scales float32 [E][rows/128][K/128], activation and h scales float32.
 struct GemmArgs {
     const uint8_t* act;        // [N][K] e4m3
-    const uint8_t* act_scale;  // [N][K/128] e8m0
+    const uint8_t* act_scale;  // [N][K/128] e8m0 (float32 for FP8 block-scaled experts)
     const int32_t* act_rows;   // optional: activation row of each expert-ordered row (gather fused into
                                // the GEMM: act/act_scale then hold one row per token); null = identity
     const int32_t* offsets;    // [E+1]
     const int32_t* tile_start; // [E+1], tiles of kRowsPerTile rows
     const int4* tile_info;     // per m-tile {expert, first row, rows}, expert -1 past the end
     const uint8_t* w;          // codes
-    const uint8_t* w_scale;    // e8m0 per 32
+    const uint8_t* w_scale;    // e8m0 per 32 (float32 per 128 x 128 block for FP8 block-scaled experts)
     void* out;                 // swiglu: hq [N][I] + hs; preact: float [N][2I]; gemm2: float [N][H]
-    uint8_t* out_scale;        // swiglu: hs [N][I/128]
+    uint8_t* out_scale;        // swiglu: hs [N][I/128] (e8m0, or float32 for FP8 block-scaled experts)
     int64_t N;
     int H, I, E;
     int packed;                // weight codes in the 16-row packed layout (moe_prepack_weights)
@@ -121,6 +133,10 @@ hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stre
 constexpr int kRowsPerTileTiled = 128;
 bool tiled_gemm_supported(int H, int I);
 hipError_t launch_expert_gemm_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream);
+
+// FP8 block-scaled experts (e4m3 weights, float32 128 x 128 block scales),
+// streaming structure, any row count.
+hipError_t launch_expert_gemm_fp8(GemmMode mode, const GemmArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y,
                           int out_bf16, int64_t T, int H, int k, hipStream_t stream);

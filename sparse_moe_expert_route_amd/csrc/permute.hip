@@ -227,11 +227,13 @@ hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, co
 // 256 threads per row, 8 channels (one 16-byte bf16 load) per thread, so a
 // 128-channel block is 16 consecutive lanes: amax by xor-shuffles within the
 // 16, then the shared block exponent, then RNE e4m3 codes of x * 2^-e
-// (an exact power-of-two scaling).
+// (an exact power-of-two scaling).  F32S (FP8 block-scaled experts): the
+// block's float32 scale amax / 448 and RNE e4m3 codes of x / scale.
 // ---------------------------------------------------------------------------
+template <bool F32S>
 __global__ void __launch_bounds__(256) quant_gather_kernel(const uint16_t* __restrict__ x,
                                                            const int32_t* __restrict__ sorted_token,
-                                                           uint8_t* __restrict__ xq, uint8_t* __restrict__ xs,
+                                                           uint8_t* __restrict__ xq, void* __restrict__ xs,
                                                            int N, int H, int T) {
     for (int r = blockIdx.x; r < N; r += gridDim.x) {
         // (no sorted_token: quantise the tokens in their own order)
@@ -250,24 +252,37 @@ __global__ void __launch_bounds__(256) quant_gather_kernel(const uint16_t* __res
             for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
             for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-            const int e = fp8_block_exponent(amax);
             float q[8];
+            if constexpr (F32S) {
+                // float32 scale amax / 448 (FP8 block-scaled experts)
+                const float sc = fp8_f32_scale(amax);
+                const float d = amax > 0.0f ? sc : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_ldexpf(v[i], -e);
+                for (int i = 0; i < 8; ++i) q[i] = fp8_f32_quotient(v[i], d);
+                if ((threadIdx.x & 15) == 0) ((float*)xs)[(size_t)r * (H / kFp8Block) + c / kFp8Block] = sc;
+            } else {
+                const int e = fp8_block_exponent(amax);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_ldexpf(v[i], -e);
+                if ((threadIdx.x & 15) == 0) ((uint8_t*)xs)[(size_t)r * (H / kFp8Block) + c / kFp8Block] = (uint8_t)(e + 127);
+            }
             uint2 codes;
             codes.x = pack_fp8x4(q[0], q[1], q[2], q[3]);
             codes.y = pack_fp8x4(q[4], q[5], q[6], q[7]);
             *(uint2*)(qr + c) = codes;
-            if ((threadIdx.x & 15) == 0) xs[(size_t)r * (H / kFp8Block) + c / kFp8Block] = (uint8_t)(e + 127);
         }
     }
 }
 
-hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq, uint8_t* xs,
-                               int64_t N, int H, int64_t T, hipStream_t stream) {
+hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq, void* xs,
+                               int64_t N, int H, int64_t T, int f32_scales, hipStream_t stream) {
     const int grid = (int)(N < 65536 ? N : 65536);
-    hipLaunchKernelGGL(quant_gather_kernel, dim3(grid), dim3(256), 0, stream, x, sorted_token, xq, xs, (int)N, H,
-                       (int)T);
+    if (f32_scales)
+        hipLaunchKernelGGL(quant_gather_kernel<true>, dim3(grid), dim3(256), 0, stream, x, sorted_token, xq, xs,
+                           (int)N, H, (int)T);
+    else
+        hipLaunchKernelGGL(quant_gather_kernel<false>, dim3(grid), dim3(256), 0, stream, x, sorted_token, xq, xs,
+                           (int)N, H, (int)T);
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ import numpy as np
 __all__ = [
     "CONFIGS", "config", "make_layer", "zipf_bias", "lib", "build",
     "philox4x32_10", "normal_f32", "bf16_normal", "mxfp4_normal", "fp8block_normal",
-    "lossless_gemm_inputs", "tie_logits", "random_ids",
+    "lossless_gemm_inputs", "lossless_fp8_gemm_inputs", "tie_logits", "random_ids",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -228,6 +228,32 @@ def lossless_gemm_inputs(rows, K, n_out, seed=0, batch=None):
     sshape = (n_out, K // 32) if batch is None else (batch, n_out, K // 32)
     w = rng.integers(0, 256, size=wshape).astype(np.uint8)
     w_s = rng.integers(126, 128, size=sshape).astype(np.uint8)
+    return a, a_s, w, w_s
+
+
+# e4m3 bit patterns with exponent field 7 (values 1 .. 1.875 in steps of 1/8),
+# either sign, plus zero
+_UNIT_E4M3 = np.array([0x00] + list(range(0x38, 0x40)) + list(range(0xB8, 0xC0)), dtype=np.uint8)
+
+
+def lossless_fp8_gemm_inputs(rows, K, n_out, seed=0, batch=None):
+    """Operands of an e4m3 x e4m3 product with float32 scales whose float32 accumulation is exact.
+
+    Activations: codes from the set above with exponent field 7 or 8 (multiples of 1/8
+    below 4), scales in {1, 2}; weights: exponent field 7 (multiples of 1/8 below 2),
+    block scales in {1, 2}.  Every term is then a multiple of 2**-6 below 32, so for
+    K <= 8192 every partial sum is a multiple of 2**-6 below 2**18: exact in binary32.
+
+    returns (a_codes [rows, K] uint8, a_scales [rows, K/128] float32,
+             w_codes [.., n_out, K] uint8, w_scales [.., n_out/128, K/128] float32)
+    """
+    rng = np.random.default_rng([seed, 78])
+    a = rng.choice(_SMALL_E4M3, size=(rows, K)).astype(np.uint8)
+    a_s = rng.integers(0, 2, size=(rows, K // 128)).astype(np.float32) + np.float32(1)
+    wshape = (n_out, K) if batch is None else (batch, n_out, K)
+    sshape = (n_out // 128, K // 128) if batch is None else (batch, n_out // 128, K // 128)
+    w = rng.choice(_UNIT_E4M3, size=wshape).astype(np.uint8)
+    w_s = rng.integers(0, 2, size=sshape).astype(np.float32) + np.float32(1)
     return a, a_s, w, w_s
 
 

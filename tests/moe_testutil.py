@@ -45,10 +45,11 @@ def weights(layer, packed=False):
     W = moe.ExpertWeights(dev(layer["w13"]), dev(layer["w13_s"]), dev(layer["w2"]), dev(layer["w2_s"]))
     if not packed:
         return W
-    T, H = layer["x"].shape
-    E, k = layer["w13"].shape[0], layer["top_k"]
-    p = moe.Problem.make(T, H, layer["w13"].shape[1] // 2, E, k)
-    return moe.prepack_weights(p, W)
+    return moe.prepack_weights(problem(layer), W)
+
+
+def is_fp8_block(layer):
+    return layer.get("format", "mxfp4") == "fp8_block"
 
 
 def pack_codes_reference(codes):
@@ -74,7 +75,8 @@ def problem(layer):
     T, H = layer["x"].shape
     E = layer["w13"].shape[0]
     inter = layer["w13"].shape[1] // 2
-    return moe.Problem.make(T, H, inter, E, layer["top_k"], 1 if layer.get("score") == "sigmoid" else 0)
+    return moe.Problem.make(T, H, inter, E, layer["top_k"], 1 if layer.get("score") == "sigmoid" else 0,
+                            moe.EXPERTS_FP8_BLOCK if is_fp8_block(layer) else moe.EXPERTS_MXFP4)
 
 
 def logit_tol(L_ref):
@@ -154,15 +156,16 @@ def _e4m3_neighbours(v):
     return q, step_up, step_dn
 
 
-def h_rounding_allowance(a, w13_e, w13_s_e, w2_e, w2_s_e, acc_rel=ACC_REL):
+def h_rounding_allowance(a, w13_e, w13_s_e, w2_e, w2_s_e, acc_rel=ACC_REL, fmt="mxfp4"):
     """Oracle-side flags of ambiguous h codes for one expert's rows, and their effect on y.
 
     a: [n, H] float64 dequantised activations.
     returns (y [n, H] oracle expert output, allow [n, H] >= 0, flags) where flags is a
     dict with the oracle's h codes/scales and boolean masks "element" [n, I] and "block" [n, I/128]."""
     from oracle import formats as F
-    W13 = F.decode_mxfp4(w13_e, w13_s_e)
-    W2 = F.decode_mxfp4(w2_e, w2_s_e)
+    from oracle import layer as OL
+    W13 = OL.decode_expert_matrix(w13_e, w13_s_e, fmt)
+    W2 = OL.decode_expert_matrix(w2_e, w2_s_e, fmt)
     inter = W13.shape[0] // 2
     gu = a @ W13.T
     S = np.abs(a) @ np.abs(W13).T
@@ -174,6 +177,8 @@ def h_rounding_allowance(a, w13_e, w13_s_e, w2_e, w2_s_e, acc_rel=ACC_REL):
     dsilu = np.abs(sig * (1.0 + g * (1.0 - sig))) + 0.25 * dg       # |d silu/dg| over the interval (|silu''| <= 1/2)
     h = silu * u
     dh = dsilu * np.abs(u) * dg + (np.abs(silu) + dsilu * dg) * du + 16 * _EPS32 * np.abs(h)
+    if fmt == "fp8_block":
+        return _h_allowance_f32(h, dh, W2)
     hq, hs = F.quantize_fp8_blocks(h)
     R, C = h.shape
     e = np.repeat(hs.astype(np.float64) - 127, 128, axis=1)
@@ -201,6 +206,36 @@ def h_rounding_allowance(a, w13_e, w13_s_e, w2_e, w2_s_e, acc_rel=ACC_REL):
     return hd @ W2.T, allow_h @ np.abs(W2).T, flags
 
 
+def _h_allowance_f32(h, dh, W2):
+    """h_rounding_allowance for float32 block scales (s = amax / 448): the GPU's scale can
+    move with its block maximum, so each element's quotient h / s is known only to an
+    interval; an element is ambiguous where that interval reaches a rounding midpoint."""
+    from oracle import formats as F
+    R, C = h.shape
+    hq, hs = F.quantize_fp8_blocks_f32(h)
+    blk = lambda z: z.reshape(R, C // 128, 128)
+    amax_hi = blk(np.abs(h) + dh).max(-1)
+    amax_lo = np.maximum(blk(np.abs(h) - dh).max(-1), 0)
+    s = np.repeat(hs.astype(np.float64), 128, axis=1)
+    s_hi = np.repeat(amax_hi / 448.0, 128, axis=1) * (1 + 4 * _EPS32) + 1e-300
+    s_lo = np.repeat(amax_lo / 448.0, 128, axis=1) * (1 - 4 * _EPS32)
+    q = np.abs(F.decode_e4m3(hq))
+    _, up, dn = _e4m3_neighbours(q)
+    v_hi = np.minimum((np.abs(h) + dh) / np.maximum(s_lo, 1e-300), 448.0 * (1 + 4 * _EPS32))
+    v_lo = np.maximum(np.abs(h) - dh, 0) / s_hi
+    cross_up = v_hi >= q + up / 2
+    cross_dn = (v_lo <= q - dn / 2) & (q > 0)
+    allow_el = np.where(cross_up, up, 0.0) + np.where(cross_dn, dn, 0.0)
+    allow_el = np.where(v_lo <= 0, np.maximum(allow_el, q + up), allow_el)
+    # a flagged element may land one grid step away, at the GPU's scale (at most s_hi);
+    # every element also carries the difference of the two scales
+    allow_h = allow_el * s_hi + q * np.maximum(s_hi - s, s - s_lo)
+    hd = F.dequantize_fp8_blocks_f32(hq, hs)
+    flags = {"hq": hq, "hs": hs, "element": allow_el > 0, "block": np.zeros((R, C // 128), bool),
+             "scale_lo": s_lo[:, ::128], "scale_hi": s_hi[:, ::128]}
+    return hd @ W2.T, allow_h @ np.abs(W2).T, flags
+
+
 def oracle_with_allowance(layer, tokens=None):
     """Oracle output of the chosen tokens (all if None) and the allowance of ambiguous h codes.
 
@@ -211,15 +246,16 @@ def oracle_with_allowance(layer, tokens=None):
     x = layer["x"] if tokens is None else layer["x"][np.asarray(tokens)]
     L = OL.router_logits(x, layer["w_router"])
     ids, w = OL.select_topk(L.astype(np.float32), k, layer.get("bias"), layer.get("score", "softmax"))
-    xq, xs = OL.quantize_activations(x)
-    a = F.dequantize_fp8_blocks(xq, xs)
+    fmt = OL.expert_format(layer)
+    xq, xs = OL.quantize_activations(x, fmt)
+    a = F.dequantize_fp8_blocks_f32(xq, xs) if fmt == "fp8_block" else F.dequantize_fp8_blocks(xq, xs)
     n, H = x.shape
     y = np.zeros((n, H))
     allow = np.zeros((n, H))
     for e in np.unique(ids):
         sel = np.argwhere(ids == e)
         ye, al, _ = h_rounding_allowance(a[sel[:, 0]], layer["w13"][e], layer["w13_s"][e], layer["w2"][e],
-                                         layer["w2_s"][e])
+                                         layer["w2_s"][e], fmt=fmt)
         wj = w[sel[:, 0], sel[:, 1]][:, None]
         np.add.at(y, sel[:, 0], wj * ye)
         np.add.at(allow, sel[:, 0], wj * al)

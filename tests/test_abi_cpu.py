@@ -37,20 +37,20 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     for st, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"), (4, b"HIP launch failure")]:
         assert lib.moe_status_string(st) == text
     assert lib.moe_status_string(99) == b"unknown status"
 
 
-def _P(T=64, H=256, I=128, E=8, k=2, sf=0):
-    return moe.Problem.make(T, H, I, E, k, sf)
+def _P(T=64, H=256, I=128, E=8, k=2, sf=0, fmt=0):
+    return moe.Problem.make(T, H, I, E, k, sf, fmt)
 
 
 @pytest.mark.parametrize("bad", [dict(H=100), dict(H=0), dict(I=64), dict(E=0), dict(E=513), dict(k=0),
-                                 dict(k=9), dict(E=4, k=5), dict(T=-1), dict(sf=2)])
+                                 dict(k=9), dict(E=4, k=5), dict(T=-1), dict(sf=2), dict(fmt=2), dict(fmt=-1)])
 def test_workspace_size_rejects_invalid_problems(lib, bad):
-    args = dict(T=64, H=256, I=128, E=8, k=2, sf=0)
+    args = dict(T=64, H=256, I=128, E=8, k=2, sf=0, fmt=0)
     args.update(bad)
     p = _P(**args)
     assert lib.moe_workspace_size(ctypes.byref(p)) == 0
@@ -63,6 +63,9 @@ def test_workspace_size_covers_intermediates(lib):
         N = T * k
         need = N * H * 4 + N * H + N * I + T * E * 4   # y_perm + x codes + h codes + logits
         assert n >= need and n % 256 == 0
+        # float32 activation and h scales with FP8 block-scaled experts
+        n8 = lib.moe_workspace_size(ctypes.byref(_P(T, H, I, E, k, 0, 1)))
+        assert n8 >= need + N * (H + I) // 128 * 4 and n8 % 256 == 0 and n8 >= n
 
 
 FAKE = 1 << 20   # an aligned non-null address; never dereferenced (every call below fails validation or is a no-op)
@@ -117,6 +120,10 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert prepack(p, w, outs[:1] + [vp(2 * M + 256)] + outs[2:]) == 1   # scales overlap the codes
     assert prepack(p, w0, outs) == 1
     assert prepack(pb, w, outs) == 1
+    # FP8 block-scaled experts: sizes of that format (w13 is 8 * 256 * 256 bytes = 512 KiB here)
+    p8 = _P(fmt=1)
+    assert prepack(p8, w, [vp(FAKE + 384 * 1024)] + outs[1:]) == 1   # inside the e4m3 w13 input
+    assert prepack(p8, wp, outs) == 1
     # unknown scoring function
     ps = _P(sf=2)
     assert lib.moe_route(ctypes.byref(ps), None, None, None, vp(FAKE), vp(FAKE), vp(FAKE), None) == 2

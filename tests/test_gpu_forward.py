@@ -1,9 +1,11 @@
 """GPU parity of the whole layer (moe_forward) against the oracle.
 
-Small layers are compared on every token; the five workloads at their full
-sizes (tiny, Flash decode/prefill, Pro decode, Pro skewed prefill) are run in
-the launch configuration the benchmark times and compared on sampled tokens
-that the oracle evaluates one by one, plus invariants over all tokens.
+Small layers are compared on every token; the workloads at their full sizes
+(tiny, Flash decode/prefill, Pro decode, Pro skewed prefill, their 4-way
+tensor-parallel shares, the speculative-verify blocks and the FP8
+block-scaled expert format) are run in the launch configuration the
+benchmark times and compared on sampled tokens that the oracle evaluates one
+by one, plus invariants over all tokens.
 
 Tokens whose top-k decision lies within the measured logit deviation of a
 tie can legitimately route differently on the GPU (float32) and in the
@@ -71,8 +73,16 @@ SMALL = [("tiny", {}, False), ("tiny", dict(bias="zipf", E=32, k=4, T=100), Fals
 SIGMOID = [("tiny", dict(T=100, E=32, k=4, bias="zipf"), False), ("tiny", dict(T=300, H=512, I=512, E=8, k=4), True),
            ("flash_decode", dict(T=16, E=32), True)]
 
+# FP8 block-scaled experts (e4m3 weights, float32 128 x 128 block scales); K not a
+# multiple of 256 (H = 384, I = 640) takes the one-step stage
+FP8 = [("tiny", dict(format="fp8_block"), False), ("tiny", dict(T=129, H=512, I=256, E=24, k=8, format="fp8_block"), True),
+       ("tiny", dict(T=40, H=1024, I=640, E=12, k=3, format="fp8_block"), False),
+       ("tiny", dict(T=300, H=384, I=384, E=8, k=8, bias="zipf", format="fp8_block"), True),
+       ("tiny", dict(T=600, H=512, I=512, E=8, k=4, format="fp8_block"), True),
+       ("tiny", dict(T=1, format="fp8_block"), True)]
 
-@pytest.mark.parametrize("cfg,over,packed", SMALL + [(c, dict(o, score="sigmoid"), pk) for c, o, pk in SIGMOID])
+
+@pytest.mark.parametrize("cfg,over,packed", SMALL + [(c, dict(o, score="sigmoid"), pk) for c, o, pk in SIGMOID] + FP8)
 def test_forward_small_parity(moe, cfg, over, packed):
     over = dict(over)
     score = over.pop("score", "softmax")
@@ -99,9 +109,9 @@ def test_forward_small_parity(moe, cfg, over, packed):
     assert np.array_equal(_forward(moe, lay, p, W), y)
 
 
-@pytest.mark.parametrize("packed", [False, True])
-def test_staged_entry_points_equal_forward(moe, packed):
-    lay = S.make_layer("tiny", seed=4, T=200, E=16, k=4, bias="zipf")
+@pytest.mark.parametrize("packed,fmt", [(False, "mxfp4"), (True, "mxfp4"), (False, "fp8_block"), (True, "fp8_block")])
+def test_staged_entry_points_equal_forward(moe, packed, fmt):
+    lay = S.make_layer("tiny", seed=4, T=200, E=16, k=4, bias="zipf", format=fmt)
     p = problem(lay)
     T, H = lay["x"].shape
     E, k, inter = p.num_experts, p.top_k, p.intermediate
@@ -118,12 +128,12 @@ def test_staged_entry_points_equal_forward(moe, packed):
     st = torch.empty(N, dtype=torch.int32, device="cuda")
     ros = torch.empty(N, dtype=torch.int32, device="cuda")
     xq = torch.empty(N, H, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(N, H // 128, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(N, H // 128, dtype=moe.scale_dtype(p), device="cuda")
     moe.permute(p, ids, x, off, st, ros, xq, xs, ws)
     yp = torch.empty(N, H, device="cuda")
     moe.grouped_gemm_swiglu(p, xq, xs, off, W, yp, ws)
     hq = torch.empty(N, inter, dtype=torch.uint8, device="cuda")
-    hs = torch.empty(N, inter // 128, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(N, inter // 128, dtype=moe.scale_dtype(p), device="cuda")
     moe.grouped_gemm1_swiglu(p, xq, xs, off, W, hq, hs, ws)
     yp2 = torch.empty(N, H, device="cuda")
     moe.grouped_gemm2(p, hq, hs, off, W, yp2, ws)
@@ -142,7 +152,10 @@ FULL = [("tiny", True), ("flash_decode", True), ("pro_decode", True), ("flash_pr
         # one GPU's share of the 4-way tensor-parallel layer (I = 512)
         ("flash_decode_tp4", True), ("pro_skewed_prefill_tp4", True),
         # speculative-decoding verify blocks (32 sequences x 8 positions)
-        ("flash_verify", True), ("pro_verify", True)]
+        ("flash_verify", True), ("pro_verify", True),
+        # FP8 block-scaled experts
+        ("flash_decode_fp8", True), ("flash_decode_fp8", False), ("pro_decode_fp8", True),
+        ("flash_prefill_fp8", True)]
 
 
 @pytest.mark.timeout(900)
@@ -193,7 +206,8 @@ def test_forward_full_size_sampled(moe, cfg, packed):
 @pytest.mark.parametrize("cfg,over,packed", [("tiny", dict(T=129, H=512, I=256, E=24, k=8), True),
                                              ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), True),
                                              ("tiny", dict(T=100, E=32, k=4), False),
-                                             ("flash_decode", dict(T=64, E=32), True)])
+                                             ("flash_decode", dict(T=64, E=32), True),
+                                             ("flash_decode", dict(T=64, E=32, format="fp8_block"), True)])
 def test_forward_graph_replay_matches_eager(moe, cfg, over, packed):
     log("graph replay %s %s packed=%s" % (cfg, over, packed))
     lay = S.make_layer(cfg, seed=5, **over)

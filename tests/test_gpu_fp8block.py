@@ -1,0 +1,219 @@
+"""GPU parity of the stages of the layer with FP8 block-scaled experts (e4m3 weights,
+one float32 scale per 128 x 128 block; activation and h scales float32 amax / 448),
+through the C ABI, against the oracle.
+
+Same bars as the MXFP4 stages (tests/moe_testutil.py): bit-exact activation
+codes and scales, bit-exact packed layout, bit-exact GEMMs on operands whose
+float32 sums are exact, and on random operands h codes that agree except
+where the oracle flags the rounding as ambiguous.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from oracle import formats as F
+from oracle import layer as OL
+from moe_testutil import dev, host, log, weights, ACC_REL, h_rounding_allowance, pack_codes_reference
+
+pytestmark = pytest.mark.gpu
+
+FMT = "fp8_block"
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import sparse_moe_expert_route_amd as m
+    m.load()
+    return m
+
+
+def _P(moe, T, H, I, E, k):
+    return moe.Problem.make(T, H, I, E, k, 0, moe.EXPERTS_FP8_BLOCK)
+
+
+@pytest.mark.parametrize("T,H,E,k,skew", [(64, 256, 8, 2, None), (300, 512, 384, 8, 2.0), (1, 128, 8, 8, None),
+                                          (2500, 384, 256, 8, None), (16384, 128, 384, 8, 1.5)])
+def test_permute_fp8_scales_bitexact(moe, T, H, E, k, skew):
+    log("permute fp8-block T=%d H=%d E=%d k=%d skew=%s" % (T, H, E, k, skew))
+    ids = S.random_ids(T, E, k, seed=T + E, skew=skew)
+    x = S.bf16_normal(6, 77, (T, H))
+    x[0, :128] = 0                                   # an all-zero block: scale 0
+    if T > 1:
+        x[1, 128 - 8:128] = np.array([0x3F80, 0xBF80, 0x0001, 0x8001, 0x7F7F, 0, 0x8000, 0x4000], dtype=np.uint16)
+        x[1, :8] = np.array([0x8000] * 8, dtype=np.uint16)
+    p = _P(moe, T, H, 128, E, k)
+    N = T * k
+    ws = moe.alloc_workspace(p)
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    st = torch.empty(N, dtype=torch.int32, device="cuda")
+    ros = torch.empty(N, dtype=torch.int32, device="cuda")
+    xq = torch.empty(N, H, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(N, H // 128, dtype=torch.float32, device="cuda")
+    moe.permute(p, dev(ids), dev(x), off, st, ros, xq, xs, ws)
+    torch.cuda.synchronize()
+    ref = OL.permutation(ids, E)
+    assert np.array_equal(host(st), ref["sorted_token"])
+    qx, sx = OL.quantize_activations(x, FMT)
+    assert sx.dtype == np.float32
+    assert np.array_equal(host(xs).view(np.uint32), sx[ref["sorted_token"]].view(np.uint32))
+    assert np.array_equal(host(xq), qx[ref["sorted_token"]])
+
+
+@pytest.mark.parametrize("H,I,E", [(256, 128, 3), (4096, 2048, 2), (384, 640, 5)])
+def test_prepack_fp8_bitexact(moe, H, I, E):
+    log("prepack fp8-block H=%d I=%d E=%d" % (H, I, E))
+    rng = np.random.default_rng(H + I + E + 1)
+    w13 = rng.integers(0, 256, size=(E, 2 * I, H), dtype=np.uint8)
+    w2 = rng.integers(0, 256, size=(E, H, I), dtype=np.uint8)
+    s13 = rng.standard_normal((E, 2 * I // 128, H // 128)).astype(np.float32)
+    s2 = rng.standard_normal((E, H // 128, I // 128)).astype(np.float32)
+    p = _P(moe, 1, H, I, E, 1)
+    Wp = moe.prepack_weights(p, moe.ExpertWeights(dev(w13), dev(s13), dev(w2), dev(s2)))
+    torch.cuda.synchronize()
+    # an e4m3 row of K bytes is packed like an MXFP4 row of 2K columns (K bytes)
+    assert np.array_equal(host(Wp.w13).reshape(-1), pack_codes_reference(w13.reshape(E * 2 * I, H)))
+    assert np.array_equal(host(Wp.w2).reshape(-1), pack_codes_reference(w2.reshape(E * H, I)))
+    assert np.array_equal(host(Wp.w13_scale), s13) and np.array_equal(host(Wp.w2_scale), s2)
+
+
+def _offsets_for(T, E, k, seed, skew=None):
+    ids = S.random_ids(T, E, k, seed=seed, skew=skew)
+    return OL.permutation(ids, E)["offsets"]
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("T,H,I,E,k,skew", [(64, 256, 128, 8, 2, None), (40, 512, 256, 16, 4, 3.0),
+                                            (9, 4096, 2048, 8, 8, None), (150, 1024, 384, 12, 3, 2.0),
+                                            (3, 6144, 256, 4, 2, None), (300, 384, 512, 8, 4, 2.0),
+                                            (5, 8192, 256, 4, 2, None)])
+def test_gemm1_preact_fp8_lossless_bitexact(moe, T, H, I, E, k, skew, packed):
+    log("gemm1 fp8-block lossless T=%d H=%d I=%d E=%d k=%d packed=%s" % (T, H, I, E, k, packed))
+    N = T * k
+    off = _offsets_for(T, E, k, seed=H + I, skew=skew)
+    a, a_s, w13, w13_s = S.lossless_fp8_gemm_inputs(N, H, 2 * I, seed=1, batch=E)
+    _, _, w2, w2_s = S.lossless_fp8_gemm_inputs(1, I, H, seed=2, batch=E)
+    p = _P(moe, T, H, I, E, k)
+    ws = moe.alloc_workspace(p)
+    W = moe.ExpertWeights(dev(w13), dev(w13_s), dev(w2), dev(w2_s))
+    if packed:
+        W = moe.prepack_weights(p, W)
+    gu = torch.full((N, 2 * I), float("nan"), dtype=torch.float32, device="cuda")
+    moe.grouped_gemm1_preact(p, dev(a), dev(a_s), dev(off), W, gu, ws)
+    torch.cuda.synchronize()
+    A = F.dequantize_fp8_blocks_f32(a, a_s)
+    ref = np.zeros((N, 2 * I))
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            ref[r0:r1] = OL.expert_gate_up(A[r0:r1], w13[e], w13_s[e], FMT)
+    assert np.array_equal(host(gu).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 8, 2), (40, 512, 256, 16, 4), (9, 4096, 2048, 8, 8),
+                                       (33, 384, 640, 5, 2), (200, 1280, 256, 16, 8), (150, 6144, 512, 8, 4)])
+def test_gemm2_fp8_lossless_bitexact(moe, T, H, I, E, k, packed):
+    log("gemm2 fp8-block lossless T=%d H=%d I=%d E=%d k=%d packed=%s" % (T, H, I, E, k, packed))
+    N = T * k
+    off = _offsets_for(T, E, k, seed=7 + H)
+    hq, hs, w2, w2_s = S.lossless_fp8_gemm_inputs(N, I, H, seed=3, batch=E)
+    _, _, w13, w13_s = S.lossless_fp8_gemm_inputs(1, H, 2 * I, seed=4, batch=E)
+    p = _P(moe, T, H, I, E, k)
+    ws = moe.alloc_workspace(p)
+    W = moe.ExpertWeights(dev(w13), dev(w13_s), dev(w2), dev(w2_s))
+    if packed:
+        W = moe.prepack_weights(p, W)
+    y = torch.full((N, H), float("nan"), dtype=torch.float32, device="cuda")
+    moe.grouped_gemm2(p, dev(hq), dev(hs), dev(off), W, y, ws)
+    torch.cuda.synchronize()
+    Hd = F.dequantize_fp8_blocks_f32(hq, hs)
+    ref = np.zeros((N, H))
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            ref[r0:r1] = Hd[r0:r1] @ F.decode_fp8_block(w2[e], w2_s[e]).T
+    assert np.array_equal(host(y).astype(np.float64), ref)
+
+
+def _permuted_activations(lay, T, E, k, seed):
+    ids = S.random_ids(T, E, k, seed=seed)
+    perm = OL.permutation(ids, E)
+    xq, xs = OL.quantize_activations(lay["x"], FMT)
+    return perm, xq[perm["sorted_token"]], xs[perm["sorted_token"]]
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(64, 4096, 2048, 8, 8), (40, 1024, 640, 12, 3), (30, 6144, 256, 6, 4),
+                                       (100, 6144, 2048, 8, 8)])
+def test_gemm1_fp8_accumulation_error_bound(moe, T, H, I, E, k):
+    """Random operands: the float32 pre-activations are within ACC_REL * sum|a_k w_k| of the
+    exact values (each 128-deep block's partial times its float32 scale product, summed)."""
+    lay = S.make_layer("tiny", seed=9, T=T, H=H, I=I, E=E, k=k, format=FMT)
+    log("gemm1 fp8-block accumulation bound T=%d H=%d I=%d E=%d" % (T, H, I, E))
+    N = T * k
+    perm, xq, xs = _permuted_activations(lay, T, E, k, 12)
+    p = _P(moe, T, H, I, E, k)
+    ws = moe.alloc_workspace(p)
+    gu = torch.empty(N, 2 * I, dtype=torch.float32, device="cuda")
+    moe.grouped_gemm1_preact(p, dev(xq), dev(xs), dev(perm["offsets"]), weights(lay), gu, ws)
+    torch.cuda.synchronize()
+    A = F.dequantize_fp8_blocks_f32(xq, xs)
+    off = perm["offsets"]
+    g = host(gu).astype(np.float64)
+    worst = 0.0
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            W = F.decode_fp8_block(lay["w13"][e], lay["w13_s"][e])
+            d = np.abs(g[r0:r1] - A[r0:r1] @ W.T) / (np.abs(A[r0:r1]) @ np.abs(W).T + 1e-300)
+            worst = max(worst, float(d.max()))
+    log("  max |g_gpu - g| / sum|a w| = %.3e (bound %.1e)" % (worst, ACC_REL))
+    assert worst <= ACC_REL
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("cfg,over", [("tiny", {}), ("tiny", dict(T=90, H=512, I=384, E=16, k=4)),
+                                      ("flash_decode", dict(E=16, T=24)), ("tiny", dict(T=400, H=512, I=512, E=8, k=4))])
+def test_gemm1_swiglu_fp8_parity(moe, cfg, over, packed):
+    lay = S.make_layer(cfg, seed=5, format=FMT, **over)
+    T, H = lay["x"].shape
+    E, k = lay["w13"].shape[0], lay["top_k"]
+    inter = lay["w13"].shape[1] // 2
+    log("gemm1 swiglu fp8-block %s %s packed=%s" % (cfg, over, packed))
+    N = T * k
+    perm, xq, xs = _permuted_activations(lay, T, E, k, 11)
+    p = _P(moe, T, H, inter, E, k)
+    ws = moe.alloc_workspace(p)
+    hq = torch.empty(N, inter, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(N, inter // 128, dtype=torch.float32, device="cuda")
+    moe.grouped_gemm1_swiglu(p, dev(xq), dev(xs), dev(perm["offsets"]), weights(lay, packed), hq, hs, ws)
+    torch.cuda.synchronize()
+    A = F.dequantize_fp8_blocks_f32(xq, xs)
+    off = perm["offsets"]
+    ref_q = np.zeros((N, inter), np.uint8)
+    ref_h = np.zeros((N, inter))
+    s_lo = np.zeros((N, inter // 128))
+    s_hi = np.zeros((N, inter // 128))
+    flag_el = np.zeros((N, inter), bool)
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            o = OL.expert_ffn(A[r0:r1], lay["w13"][e], lay["w13_s"][e], lay["w2"][e], lay["w2_s"][e], FMT)
+            ref_q[r0:r1], ref_h[r0:r1] = o["hq"], o["h"]
+            _, _, fl = h_rounding_allowance(A[r0:r1], lay["w13"][e], lay["w13_s"][e], lay["w2"][e],
+                                            lay["w2_s"][e], fmt=FMT)
+            flag_el[r0:r1], s_lo[r0:r1], s_hi[r0:r1] = fl["element"], fl["scale_lo"], fl["scale_hi"]
+    gq, gs = host(hq), host(hs).astype(np.float64)
+    # every scale lies in the interval the accumulation error allows
+    assert np.all((gs >= s_lo) & (gs <= s_hi))
+    gv, rv = F.decode_e4m3(gq), F.decode_e4m3(ref_q)
+    frac_exact = np.mean(gv == rv)
+    differ = gv != rv
+    log("  exact h codes: %.5f; differing %d, flagged %d, all differing flagged: %s"
+        % (frac_exact, differ.sum(), flag_el.sum(), bool(np.all(flag_el[differ]))))
+    assert frac_exact > 0.99
+    assert np.all(flag_el[differ])
+    # the block maximum is coded as +-448 in every non-zero block
+    bmax = np.abs(gv).reshape(N, inter // 128, 128).max(-1)
+    assert np.all(bmax[gs > 0] == 448.0)

@@ -321,7 +321,7 @@ def _pins_pass(syngen):
 
 
 def test_mxfp4_nibble_pin():
-    # element 0 of a row is the low nibble of byte 0 (reading of "two 4-bit values per byte")
+    # element 0 of a row is the low nibble of byte 0 (the reading of two e2m1 values per byte)
     v = F.decode_mxfp4(np.array([[0x71] + [0] * 15], dtype=np.uint8), np.array([[127]], dtype=np.uint8))
     assert v[0, 0] == 0.5 and v[0, 1] == 6.0
 
