@@ -168,17 +168,20 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const void* act_sca
 // depends on host-known sizes only, so both GEMMs of one call agree on it.
 // The tiled kernel addresses activations with 32-bit offsets: every
 // activation matrix it reads ([T*k][H] or [T][H], [T*k][I]) stays under 2 GiB.
-// FP8 block-scaled experts always take their own streaming kernel.
+// FP8 block-scaled experts have their own pair of kernels, chosen the same way.
 bool use_tiled(const moe_problem& p) {
     const int64_t rows = p.num_tokens * p.top_k;
     const int64_t widest = p.hidden > p.intermediate ? p.hidden : p.intermediate;
-    return !fp8_block(p) && tiled_gemm_supported(p.hidden, p.intermediate) && rows >= 32 * (int64_t)p.num_experts &&
-           rows * widest < ((int64_t)1 << 31);
+    const bool shape_ok = fp8_block(p) ? fp8_tiled_gemm_supported(p.hidden, p.intermediate)
+                                       : tiled_gemm_supported(p.hidden, p.intermediate);
+    return shape_ok && rows >= 32 * (int64_t)p.num_experts && rows * widest < ((int64_t)1 << 31);
 }
 
 moe_status launch_gemm(const moe_problem& p, GemmMode mode, const GemmArgs& a, hipStream_t stream) {
-    if (fp8_block(p)) MOE_LAUNCH(launch_expert_gemm_fp8(mode, a, stream));
-    else MOE_LAUNCH(use_tiled(p) ? launch_expert_gemm_tiled(mode, a, stream) : launch_expert_gemm(mode, a, stream));
+    if (fp8_block(p))
+        MOE_LAUNCH(use_tiled(p) ? launch_expert_gemm_fp8_tiled(mode, a, stream) : launch_expert_gemm_fp8(mode, a, stream));
+    else
+        MOE_LAUNCH(use_tiled(p) ? launch_expert_gemm_tiled(mode, a, stream) : launch_expert_gemm(mode, a, stream));
     return MOE_OK;
 }
 

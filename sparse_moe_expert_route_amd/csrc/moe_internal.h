@@ -137,6 +137,9 @@ hipError_t launch_expert_gemm_tiled(GemmMode mode, const GemmArgs& a, hipStream_
 // FP8 block-scaled experts (e4m3 weights, float32 128 x 128 block scales),
 // streaming structure, any row count.
 hipError_t launch_expert_gemm_fp8(GemmMode mode, const GemmArgs& a, hipStream_t stream);
+// ... LDS-tiled for many rows per expert: m-tiles of 128 rows, H and I multiples of 512, at most 8192.
+bool fp8_tiled_gemm_supported(int H, int I);
+hipError_t launch_expert_gemm_fp8_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y,
                           int out_bf16, int64_t T, int H, int k, hipStream_t stream);

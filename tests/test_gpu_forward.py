@@ -82,7 +82,8 @@ FP8 = [("tiny", dict(format="fp8_block"), False), ("tiny", dict(T=129, H=512, I=
        ("tiny", dict(T=1, format="fp8_block"), True)]
 
 
-@pytest.mark.parametrize("cfg,over,packed", SMALL + [(c, dict(o, score="sigmoid"), pk) for c, o, pk in SIGMOID] + FP8)
+@pytest.mark.parametrize("cfg,over,packed", SMALL + [(c, dict(o, score="sigmoid"), pk) for c, o, pk in SIGMOID] +
+                         [pytest.param(c, o, pk, id="fp8_block-%d" % i) for i, (c, o, pk) in enumerate(FP8)])
 def test_forward_small_parity(moe, cfg, over, packed):
     over = dict(over)
     score = over.pop("score", "softmax")
@@ -207,7 +208,8 @@ def test_forward_full_size_sampled(moe, cfg, packed):
                                              ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), True),
                                              ("tiny", dict(T=100, E=32, k=4), False),
                                              ("flash_decode", dict(T=64, E=32), True),
-                                             ("flash_decode", dict(T=64, E=32, format="fp8_block"), True)])
+                                             pytest.param("flash_decode", dict(T=64, E=32, format="fp8_block"), True,
+                                                          id="fp8_block-flash_decode")])
 def test_forward_graph_replay_matches_eager(moe, cfg, over, packed):
     log("graph replay %s %s packed=%s" % (cfg, over, packed))
     lay = S.make_layer(cfg, seed=5, **over)
