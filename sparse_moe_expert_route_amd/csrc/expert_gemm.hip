@@ -322,8 +322,8 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float g0 = acc[0][i], g1 = acc[1][i];
-            h[i] = g0 / (1.0f + __expf(-g0)) * acc[2][i];
-            h[4 + i] = g1 / (1.0f + __expf(-g1)) * acc[3][i];
+            h[i] = silu_f32(g0) * acc[2][i];
+            h[4 + i] = silu_f32(g1) * acc[3][i];
         }
         float amax = 0.0f;
 #pragma unroll

@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float gv = acc[j][i];
-                    const float h = gv / (1.0f + __expf(-gv)) * acc[j][i + 8];
+                    const float h = silu_f32(gv) * acc[j][i + 8];
                     acc[j][i] = h;
                     m = fmaxf(m, fabsf(h));
                 }

@@ -477,7 +477,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const float gv = acc[t][j][i];
-                        const float h = gv / (1.0f + __expf(-gv)) * acc[t][j][i + 8];
+                        const float h = silu_f32(gv) * acc[t][j][i + 8];
                         acc[t][j][i] = h;
                         m = fmaxf(m, fabsf(h));
                     }

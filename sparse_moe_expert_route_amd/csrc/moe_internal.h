@@ -49,6 +49,12 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
     return (uint32_t)r;
 }
 
+// silu(z) = z / (1 + e^-z), with the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: a few ulp) instead of the correctly rounded
+// division sequence, which cost the SwiGLU epilogues about ten instructions
+// per element.  e^-z overflowing to +inf gives -0, as the division would.
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b16) {
     return __uint_as_float(b16 << 16);
 }
