@@ -15,22 +15,25 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     float ws[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        rows[j] = j < k ? row_of_slot[(size_t)t * k + j] : -1;
+        rows[j] = row_of_slot[(size_t)t * k + min(j, k - 1)];
         ws[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
     }
     // workgroup (t, b) covers channels [1024 b, 1024 b + 1024): a decode step
-    // with few tokens still spreads over the whole chip
+    // with few tokens still spreads over the whole chip.  All eight loads are
+    // issued before the first FMA (slots past k re-read slot k-1 with weight
+    // 0, which leaves the sum unchanged but for the sign of an all-zero sum),
+    // and they bypass the caches: y_perm is read once.
     for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < H; c += gridDim.y * 256 * 4) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
+        v4f v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load((const v4f*)(y_perm + (size_t)rows[j] * H + c));
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            if (j < k && rows[j] >= 0) {
-                const v4f v = *(const v4f*)(y_perm + (size_t)rows[j] * H + c);
-                acc[0] = fmaf(ws[j], v[0], acc[0]);
-                acc[1] = fmaf(ws[j], v[1], acc[1]);
-                acc[2] = fmaf(ws[j], v[2], acc[2]);
-                acc[3] = fmaf(ws[j], v[3], acc[3]);
-            }
+            acc[0] = fmaf(ws[j], v[j][0], acc[0]);
+            acc[1] = fmaf(ws[j], v[j][1], acc[1]);
+            acc[2] = fmaf(ws[j], v[j][2], acc[2]);
+            acc[3] = fmaf(ws[j], v[j][3], acc[3]);
         }
         if (out_bf16) {
             uint2 o;
