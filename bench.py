@@ -61,6 +61,7 @@ GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm.hip",
                 "sparse_moe_expert_route_amd/csrc/expert_gemm_tiled.hip",
                 "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
 FP8_GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm_fp8.hip",
+                    "sparse_moe_expert_route_amd/csrc/expert_gemm_fp8_tiled.hip",
                     "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
 
 
@@ -225,10 +226,9 @@ def main():
                 "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
     roof["traffic"] = None if args.canonical_weights else \
         measured_traffic(args.config, FP8_GEMM_SOURCES if fp8 else GEMM_SOURCES)
-    tiled = not fp8 and N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= 6144
-    roof["kernel"] = ("expert_gemm_fp8_stream_kernel" if fp8 else
-                      "expert_gemm_tiled_kernel" if tiled else "expert_gemm_stream_kernel") + \
-        "<gate/up + SwiGLU + FP8 requant>"
+    tiled = N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= (8192 if fp8 else 6144)
+    roof["kernel"] = "expert_gemm_%s%s_kernel<gate/up + SwiGLU + FP8 requant>" % ("fp8_" if fp8 else "",
+                                                                                   "tiled" if tiled else "stream")
     roof["launch_ms"] = round(gemm1_ms, 4)
     roof["algorithmic_bytes"] = int(gemm1_bytes)
     roof["algorithmic_flops"] = gemm1_flops
