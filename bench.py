@@ -13,6 +13,8 @@ Prints ONE JSON line:
                MFMA-bound) per launch / mean launch duration, against the
                MI355X peak; traffic = HBM bytes per launch from the counter
                summaries in profiles/ while the GEMM sources are unchanged
+  cold_cache_step  per-step HIP-event times of moe_forward with a 1 GiB cache
+               flush before each step (median, p10, p90)
   graph_replay the same step captured once as a HIP graph and replayed
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 Workloads: tiny, flash_decode (default), flash_prefill, pro_decode,
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the cold-cache per-step timing (1 GiB cache flush before each step)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens for the CPU oracle (0 = auto)")
     ap.add_argument("--canonical-weights", action="store_true",
                     help="run on the canonical (row-major) weight layout instead of the packed one")
@@ -155,6 +159,27 @@ def main():
     tokens_per_s = T * args.steps / wall
     log("bench: %.3f ms/step, %.0f tokens/s" % (ms_per_step, tokens_per_s))
 
+    # ---- per-step times with cold caches: before each step a 1 GiB write evicts the
+    # L2s and the 256 MB last-level cache, then HIP events bracket moe_forward alone ----
+    flushed = None
+    if not args.no_flush:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        times = []
+        for _ in range(args.steps):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            moe.forward(p, x, wr, bias, W, y, ws)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        q = np.percentile(np.array(times), [10, 50, 90])
+        flushed = {"ms_p10": round(float(q[0]), 4), "ms_median": round(float(q[1]), 4),
+                   "ms_p90": round(float(q[2]), 4), "value_median": round(T / (float(q[1]) * 1e-3), 1)}
+        log("bench: cold-cache step median %.3f ms (p10 %.3f, p90 %.3f)" % (q[1], q[0], q[2]))
+
     # ---- the same step captured once as a HIP graph and replayed (no launch overhead) ----
     graph = None
     if not args.no_graph:
@@ -253,6 +278,7 @@ def main():
                       "bias": cfg["bias"], "experts": cfg["format"]},
            "roofline": roof, "layer": layer,
            "graph_replay": graph,
+           "cold_cache_step": flushed,
            "weight_layout": "canonical" if args.canonical_weights else "packed",
            "prepack_ms": None if prepack_ms is None else round(prepack_ms, 3)}
 
