@@ -79,7 +79,10 @@ FP8 = [("tiny", dict(format="fp8_block"), False), ("tiny", dict(T=129, H=512, I=
        ("tiny", dict(T=40, H=1024, I=640, E=12, k=3, format="fp8_block"), False),
        ("tiny", dict(T=300, H=384, I=384, E=8, k=8, bias="zipf", format="fp8_block"), True),
        ("tiny", dict(T=600, H=512, I=512, E=8, k=4, format="fp8_block"), True),
-       ("tiny", dict(T=1, format="fp8_block"), True)]
+       ("tiny", dict(T=1, format="fp8_block"), True),
+       # sigmoid scoring with FP8 block-scaled experts, streaming and tiled kernels
+       ("tiny", dict(T=100, E=32, k=4, bias="zipf", format="fp8_block", score="sigmoid"), True),
+       ("tiny", dict(T=600, H=512, I=512, E=8, k=4, format="fp8_block", score="sigmoid"), False)]
 
 
 @pytest.mark.parametrize("cfg,over,packed", SMALL + [(c, dict(o, score="sigmoid"), pk) for c, o, pk in SIGMOID] +
