@@ -46,18 +46,23 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
 
     const int kspan = H / KS;
     const int kbeg = ks * kspan, kend = kbeg + kspan;
-    // kspan is a multiple of 32; unroll by 4 steps of 32 where possible
+    // kspan is a multiple of 32.  Chunks of 16 steps of 32: the 32 loads of a
+    // chunk go out together, so a decode-sized K range costs two or three
+    // memory round trips rather than one per step (same MFMA order, so the
+    // same sums).
     int kk = kbeg;
-    for (; kk + 128 <= kend; kk += 128) {
-        v8bf a[4], b[4][TT];
+    constexpr int U = 16;
+    for (; kk + 32 * U <= kend; kk += 32 * U) {
+        v8bf a[U], b[U][TT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             a[u] = *(const v8bf*)(wp + kk + 32 * u + 8 * g);
 #pragma unroll
             for (int j = 0; j < TT; ++j) b[u][j] = *(const v8bf*)(xp[j] + kk + 32 * u + 8 * g);
         }
+        __builtin_amdgcn_sched_barrier(0);   // every load of the chunk before its first MFMA
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < TT; ++j)
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b[u][j], acc[j], 0, 0, 0);
