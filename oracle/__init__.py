@@ -16,10 +16,10 @@ Sources (the pages; cited by page title and section):
     "What Did Xiaomi Release?" (routed experts 256/8 and 384/8),
     "How Big Is Each Expert?" (router picks 8 experts; gate/up/down around a
     2,048-wide middle), "Why Are the V2.6 Files Half the Size of V2.5?"
-    (MXFP4: two 4-bit values per byte, one 8-bit scale per 32 values;
+    (MXFP4: a byte holds two e2m1 codes, and each run of 32 values shares one e8m0 scale;
     BF16 router), "How Is the Backbone Built?" (no shared expert).
   * vLLM recipe "XiaomiMiMo/MiMo-V2.6-Pro-RL", section "Overview"
-    (stored as mxfp4, computed as FP8 block-wise e4m3).
+    (experts stored in MXFP4, the arithmetic done in block-scaled e4m3).
   * devupai.com "MiMo-V2.6-Flash", sections "No shared expert" and
     "Self-Hosting" (dynamic activation scheme).
 

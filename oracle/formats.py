@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Formats (the teardown page, "Why Are the V2.6 Files Half the Size of V2.5?",
 table row "Routed experts"; the vLLM recipe, "Overview"):
-  * MXFP4 expert weights: two 4-bit values per byte, one 8-bit scale for each
-    group of 32 values.  The 4-bit value is OCP e2m1, the 8-bit scale is OCP
+  * MXFP4 expert weights: each byte holds two 4-bit codes, and each group of
+    32 values shares one 8-bit scale.  The 4-bit value is OCP e2m1, the scale is OCP
     e8m0 (a bare power of two).  Which nibble holds which element is not on
     the pages; the reading used here is element 2i in bits 3:0 and element
     2i+1 in bits 7:4.

@@ -12,7 +12,7 @@ What the layer is (the pages, by section):
     there is no shared expert, so the output is the routed sum alone;
   * teardown "Why Are the V2.6 Files Half the Size of V2.5?": experts are
     stored as MXFP4, the router is BF16;
-  * vLLM recipe "Overview": computed as FP8 e4m3, block-wise;
+  * vLLM recipe "Overview": the arithmetic runs in block-scaled FP8 e4m3;
   * teardown "Why Are the V2.6 Files Half the Size of V2.5?", V2.5 column:
     the earlier expert format, FP8 e4m3 with one float32 scale per 128 x 128
     block (layer["format"] == "fp8_block").
