@@ -62,8 +62,8 @@ typedef enum {
  *   k selected logits L (the measured workloads).
  * MOE_SCORE_SIGMOID_BIAS: s = sigmoid(L) = 1 / (1 + e^-L) in fp32;
  *   key = s + b (fp32 add); weights = the k selected s divided by their sum
- *   (teardown "How Big Is Each Expert?": experts scored with a sigmoid plus a
- *   small per-expert correction bias that keeps the load spread).
+ *   (teardown "How Big Is Each Expert?": sigmoid expert scores, plus a
+ *   per-expert bias that balances the load across experts).
  * In both, b steers only the selection, ties go to the lower expert id.  */
 typedef enum { MOE_SCORE_SOFTMAX_TOPK = 0, MOE_SCORE_SIGMOID_BIAS = 1 } moe_score_func;
 
@@ -193,9 +193,9 @@ moe_status moe_permute(const moe_problem* problem, const int32_t* topk_ids, cons
                        hipStream_t stream);
 
 /* The experts on their rows: gate/up projection, SwiGLU, FP8 requantisation
- * of h, down projection (teardown, "How Big Is Each Expert?": gate, up and
- * down projections around a 2,048-wide middle; vLLM recipe "Overview": FP8
- * compute of MXFP4-stored weights).
+ * of h, down projection (teardown, "How Big Is Each Expert?": each expert is
+ * a gate, an up and a down matrix with an intermediate width of 2,048; vLLM
+ * recipe "Overview": MXFP4-stored weights, FP8 arithmetic).
  *   xq_perm, xs_perm, expert_offsets  as produced by moe_permute
  *   y_perm [T*k][H] fp32 out: expert output of each row (unweighted)       */
 moe_status moe_grouped_gemm_swiglu(const moe_problem* problem, const uint8_t* xq_perm,

@@ -14,8 +14,8 @@ one the definition itself states (SwiGLU between the two projections).
 Sources (the pages; cited by page title and section):
   * "MiMo V2.6 Pro and Flash architecture teardown" (kgptalkie.com), sections
     "What Did Xiaomi Release?" (routed experts 256/8 and 384/8),
-    "How Big Is Each Expert?" (router picks 8 experts; gate/up/down around a
-    2,048-wide middle), "Why Are the V2.6 Files Half the Size of V2.5?"
+    "How Big Is Each Expert?" (router picks 8 experts; gate, up and down
+    matrices, intermediate width 2,048), "Why Are the V2.6 Files Half the Size of V2.5?"
     (MXFP4: a byte holds two e2m1 codes, and each run of 32 values shares one e8m0 scale;
     BF16 router), "How Is the Backbone Built?" (no shared expert).
   * vLLM recipe "XiaomiMiMo/MiMo-V2.6-Pro-RL", section "Overview"

@@ -111,8 +111,8 @@ def select_topk(logits, k, bias=None, score="softmax"):
     binary32 addition); the weights are a softmax over the k selected
     *unbiased* logits, computed in float64 with the maximum subtracted.
 
-    score="sigmoid" (teardown "How Big Is Each Expert?": a sigmoid score plus
-    a small per-expert correction bias): s = sigmoid(L) rounded to float32;
+    score="sigmoid" (teardown "How Big Is Each Expert?": sigmoid scores and a
+    per-expert load-balancing bias): s = sigmoid(L) rounded to float32;
     the key is the float32 sum s + b; the weights are the k selected scores
     (float64) divided by their sum.
 

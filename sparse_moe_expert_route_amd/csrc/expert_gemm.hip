@@ -1,10 +1,10 @@
 // Grouped expert GEMMs on the gfx950 block-scaled MFMA
 // (v_mfma_scale_f32_16x16x128_f8f6f4), A = MXFP4 weights, B = FP8 activations.
 //
-// Experts are gate/up/down projections around a 2,048-wide middle (teardown,
-// "How Big Is Each Expert?"), stored as MXFP4 ("Why Are the V2.6 Files Half
+// Experts are gate, up and down matrices with an intermediate width of 2,048
+// (teardown, "How Big Is Each Expert?"), stored as MXFP4 ("Why Are the V2.6 Files Half
 // the Size of V2.5?") and computed in FP8 e4m3 (vLLM recipe, "Overview").
-// MXFP4 runs natively on CDNA 4 (vLLM recipe, "AMD (MI355X, TP4)"), so the
+// CDNA 4 executes MXFP4 directly (vLLM recipe, "AMD (MI355X, TP4)"), so the
 // e2m1 codes and their e8m0 scales go to the MFMA as stored.
 //
 // Operand layout of the 16x16x128 instruction (lane l, g = l/16, r = l%16):

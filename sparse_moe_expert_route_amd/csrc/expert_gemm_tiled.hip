@@ -3,8 +3,8 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4), A = MXFP4 weights, B = FP8 activations.
 //
 // Same computation as the streaming kernel (expert_gemm.hip): experts are
-// gate/up/down projections around a 2,048-wide middle (teardown, "How Big Is
-// Each Expert?"), stored as MXFP4 and computed in FP8 e4m3 (vLLM recipe,
+// gate, up and down matrices with an intermediate width of 2,048 (teardown,
+// "How Big Is Each Expert?"), stored as MXFP4 and computed in FP8 e4m3 (vLLM recipe,
 // "Overview"); e2m1 codes and e8m0 scales go to the MFMA as stored.
 //
 // Operand layout of the 32x32x64 instruction (lane l, g = l/32, r = l%32):

@@ -277,8 +277,8 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// SIG: sigmoid scoring (teardown "How Big Is Each Expert?": the router scores
-// experts with a sigmoid and adds a small per-expert correction bias):
+// SIG: sigmoid scoring (teardown "How Big Is Each Expert?": sigmoid expert
+// scores and a per-expert load-balancing bias):
 // key = fp32(sigmoid(L) + b), weights = sigmoid of the selected logits over
 // their sum.  Otherwise softmax scoring as above.
 template <int EJ, bool SIG>
