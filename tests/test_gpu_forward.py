@@ -67,7 +67,11 @@ SMALL = [("tiny", {}, False), ("tiny", dict(bias="zipf", E=32, k=4, T=100), Fals
          ("tiny", dict(T=512, H=512, I=512, E=16, k=4, bias="zipf"), True),
          ("tiny", dict(T=400, H=1024, I=1536, E=16, k=8), True),
          # at most 1024 slots (single-workgroup permutation) on the tiled kernel
-         ("tiny", dict(T=100, H=512, I=512, E=8, k=4), True)]
+         ("tiny", dict(T=100, H=512, I=512, E=8, k=4), True),
+         # the largest expert count (512: eight keys per lane in the top-k)
+         ("tiny", dict(T=100, H=512, I=256, E=512, k=8), True),
+         # H above the tiled kernel's limit: many rows per expert on the streaming kernel
+         ("tiny", dict(T=300, H=8192, I=256, E=8, k=4), True)]
 
 
 SIGMOID = [("tiny", dict(T=100, E=32, k=4, bias="zipf"), False), ("tiny", dict(T=300, H=512, I=512, E=8, k=4), True),
