@@ -164,7 +164,9 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
     const int within = local - kMChunk * NB * chunk;
     const int nblk = within / cs;
     const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
-    return Item{e, ti.y, ti.z, nblk};
+    // every lane computes the same item: keep it in scalar registers
+    return Item{__builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(ti.y),
+                __builtin_amdgcn_readfirstlane(ti.z), __builtin_amdgcn_readfirstlane(nblk)};
 }
 
 // The persistent loop of one workgroup.  LDS buffers come in as restrict
@@ -176,7 +178,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                                            uint8_t* __restrict__ act2, uint8_t* __restrict__ act3,
                                            uint8_t* __restrict__ xsc, float* __restrict__ red) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, r = lane & 31;
 
     const int K = (MODE == kGemm2) ? a.I : a.H;
@@ -436,23 +438,23 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         if constexpr (MODE == kGemm2) {
 #pragma unroll
             for (int j = 0; j < kTT; ++j) {
-                const int rr = 32 * j + r;
-                if (rr >= nrows) continue;
-                float* o = (float*)a.out + (size_t)(row0 + rr) * a.H + nblk * kItemRows + 32 * kWT * wave + 4 * g;
+                // uniform base plus a 32-bit lane offset
+                if (r >= nrows - 32 * j) continue;
+                float* ob = (float*)a.out + ((size_t)(row0 + 32 * j) * a.H + nblk * kItemRows + 32 * kWT * wave);
+                const uint32_t lo = (uint32_t)(r * a.H + 4 * g);
 #pragma unroll
                 for (int t = 0; t < kWT; ++t)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *(v4f*)(o + 32 * t + 8 * q) =
+                        *(v4f*)(ob + (lo + 32 * t + 8 * q)) =
                             v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2], acc[t][j][4 * q + 3]};
             }
         } else if constexpr (MODE == kGemm1Preact) {
             // tile row 8q + 4g + i: q = 0, 1 gate features f + 8q + 4g + i, q = 2, 3 up
 #pragma unroll
             for (int j = 0; j < kTT; ++j) {
-                const int rr = 32 * j + r;
-                if (rr >= nrows) continue;
-                float* o = (float*)a.out + (size_t)(row0 + rr) * (2 * a.I);
+                if (r >= nrows - 32 * j) continue;
+                float* o = (float*)a.out + (size_t)(row0 + 32 * j) * (2 * a.I) + (uint32_t)(r * 2 * a.I);
 #pragma unroll
                 for (int t = 0; t < kWT; ++t) {
                     const int f = nblk * (kItemRows / 2) + 16 * kWT * wave + 16 * t;
@@ -511,9 +513,9 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                 const uint32_t x0 = g ? dw[0][0] : dw[1][0], x1 = g ? dw[0][1] : dw[1][1];
                 const uint32_t y0 = __shfl_xor(x0, 32, 64), y1 = __shfl_xor(x1, 32, 64);
                 const uint4 v = g ? uint4{y0, dw[1][0], y1, dw[1][1]} : uint4{dw[0][0], y0, dw[0][1], y1};
-                if (rr < nrows) {
-                    uint8_t* q = (uint8_t*)a.out + (size_t)(row0 + rr) * a.I + nblk * (kItemRows / 2) + 16 * kWT * wave + 16 * g;
-                    *(uint4*)q = v;
+                if (r < nrows - 32 * j) {
+                    uint8_t* qb = (uint8_t*)a.out + ((size_t)(row0 + 32 * j) * a.I + nblk * (kItemRows / 2) + 16 * kWT * wave);
+                    *(uint4*)(qb + (uint32_t)(r * a.I + 16 * g)) = v;
                     if (wave % kBlkWaves == 0 && g == 0)
                         a.out_scale[(size_t)(row0 + rr) * (a.I / kFp8Block) + 2 * nblk + wave / kBlkWaves] = (uint8_t)(ex + 127);
                 }
