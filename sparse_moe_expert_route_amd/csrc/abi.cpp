@@ -191,8 +191,10 @@ moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, con
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
     int4* ti = at<int4>(ws, L.tile_info);
-    const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
-    if (plan)
+    // only the tiled kernels read a tile plan; the streaming ones find their
+    // m-tile from the offsets
+    const int rpt = kRowsPerTileTiled;
+    if (plan && use_tiled(p))
         MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
                                     max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
     GemmArgs a = gemm_args(p, xq, xs, offsets, ts, ti, wt.w13, wt.w13_scale, out, out_scale);
@@ -206,8 +208,10 @@ moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const void* hs, co
     const Layout L = layout_of(p);
     int32_t* ts = at<int32_t>(ws, L.tile_start);
     int4* ti = at<int4>(ws, L.tile_info);
-    const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
-    if (plan)
+    // only the tiled kernels read a tile plan; the streaming ones find their
+    // m-tile from the offsets
+    const int rpt = kRowsPerTileTiled;
+    if (plan && use_tiled(p))
         MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
                                     max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
     GemmArgs a = gemm_args(p, hq, hs, offsets, ts, ti, wt.w2, wt.w2_scale, y_perm, nullptr);

@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     const int g = lane >> 4, r = lane & 15;
 
     // ---- m-tile: expert, first row, rows ----
-    const int4 ti = a.tile_info[blockIdx.y];
+    const int4 ti = find_stream_tile(a.offsets, a.E, blockIdx.y);
     if (ti.x < 0) return;   // past the last m-tile
     const int e = ti.x, row0 = ti.y, nrows = ti.z;
 

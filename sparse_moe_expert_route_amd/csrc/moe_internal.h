@@ -121,8 +121,8 @@ struct GemmArgs {
     const int32_t* act_rows;   // optional: activation row of each expert-ordered row (gather fused into
                                // the GEMM: act/act_scale then hold one row per token); null = identity
     const int32_t* offsets;    // [E+1]
-    const int32_t* tile_start; // [E+1], tiles of kRowsPerTile rows
-    const int4* tile_info;     // per m-tile {expert, first row, rows}, expert -1 past the end
+    const int32_t* tile_start; // tiled kernels: [E+1], first m-tile of each expert
+    const int4* tile_info;     // tiled kernels: per m-tile {expert, first row, rows}, expert -1 past the end
     const uint8_t* w;          // codes
     const uint8_t* w_scale;    // e8m0 per 32 (float32 per 128 x 128 block for FP8 block-scaled experts)
     void* out;                 // swiglu: hq [N][I] + hs; preact: float [N][2I]; gemm2: float [N][H]
@@ -133,6 +133,52 @@ struct GemmArgs {
 };
 constexpr int kRowsPerTile = 16;   // rows per m-tile of the streaming expert GEMM
 hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream);
+
+// M-tile t of kRowsPerTile rows, looked up from the expert offsets alone
+// (expert e owns ceil(n_e / 16) tiles, in expert order), so the streaming
+// GEMMs need no tile plan.  One wave: lane l sums the tiles of its run of
+// ceil(E/64) <= 8 experts, a wave scan finds the lane whose run holds t, and
+// that lane's walk over its run gives the expert.  Every lane returns the
+// same {expert, first row, rows, 0}, expert -1 for t past the last tile.
+// Needs E <= 512.
+__device__ __forceinline__ int4 find_stream_tile(const int32_t* __restrict__ offsets, int E, int t) {
+    const int lane = threadIdx.x & 63;
+    const int c = (E + 63) >> 6;
+    const int e0 = min(lane * c, E), e1 = min(e0 + c, E);
+    int o[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) o[i] = (e0 + i <= e1) ? offsets[e0 + i] : 0;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (e0 + i < e1) n += (o[i + 1] - o[i] + kRowsPerTile - 1) / kRowsPerTile;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    const int total = __shfl(incl, 63, 64);
+    if (t >= total) return int4{-1, 0, 0, 0};
+    const int excl = incl - n;
+    int e = -1, row0 = 0, rows = 0, before = excl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (e0 + i < e1) {
+            const int nt = (o[i + 1] - o[i] + kRowsPerTile - 1) / kRowsPerTile;
+            if (t >= before && t < before + nt) {
+                e = e0 + i;
+                row0 = o[i] + (t - before) * kRowsPerTile;
+                rows = min(kRowsPerTile, o[i + 1] - row0);
+            }
+            before += nt;
+        }
+    }
+    // exactly one lane's run holds t (runs without tiles are empty ranges)
+    const int src = __builtin_ctzll(__ballot(e >= 0));
+    return int4{__builtin_amdgcn_readfirstlane(__shfl(e, src, 64)), __builtin_amdgcn_readfirstlane(__shfl(row0, src, 64)),
+                __builtin_amdgcn_readfirstlane(__shfl(rows, src, 64)), 0};
+}
 
 // LDS-tiled variant for many rows per expert: m-tiles of 128 rows, needs
 // H and I multiples of 512, at most 6144.
