@@ -94,7 +94,7 @@ def measured_traffic(workload, sources):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the layer's expert set fits one "
+        print("bench.py measures one GPU: the library has no multi-GPU path (one layer's expert set fits one "
               "MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
