@@ -71,7 +71,11 @@ SMALL = [("tiny", {}, False), ("tiny", dict(bias="zipf", E=32, k=4, T=100), Fals
          # the largest expert count (512: eight keys per lane in the top-k)
          ("tiny", dict(T=100, H=512, I=256, E=512, k=8), True),
          # H above the tiled kernel's limit: many rows per expert on the streaming kernel
-         ("tiny", dict(T=300, H=8192, I=256, E=8, k=4), True)]
+         ("tiny", dict(T=300, H=8192, I=256, E=8, k=4), True),
+         # expert counts that are not a multiple of 64: the streaming kernels' m-tile
+         # lookup gives lanes uneven runs of experts, some none
+         ("tiny", dict(T=64, E=65, k=8), True), ("tiny", dict(T=100, H=512, I=256, E=200, k=8), False),
+         ("tiny", dict(T=3, E=130, k=8), True)]
 
 
 SIGMOID = [("tiny", dict(T=100, E=32, k=4, bias="zipf"), False), ("tiny", dict(T=300, H=512, I=512, E=8, k=4), True),
@@ -84,6 +88,7 @@ FP8 = [("tiny", dict(format="fp8_block"), False), ("tiny", dict(T=129, H=512, I=
        ("tiny", dict(T=300, H=384, I=384, E=8, k=8, bias="zipf", format="fp8_block"), True),
        ("tiny", dict(T=600, H=512, I=512, E=8, k=4, format="fp8_block"), True),
        ("tiny", dict(T=1, format="fp8_block"), True),
+       ("tiny", dict(T=50, E=100, k=6, format="fp8_block"), True),
        # sigmoid scoring with FP8 block-scaled experts, streaming and tiled kernels
        ("tiny", dict(T=100, E=32, k=4, bias="zipf", format="fp8_block", score="sigmoid"), True),
        ("tiny", dict(T=600, H=512, I=512, E=8, k=4, format="fp8_block", score="sigmoid"), False)]

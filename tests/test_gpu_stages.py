@@ -212,7 +212,9 @@ def test_prepack_bitexact(moe, H, I, E):
                                             (3, 6144, 256, 4, 2, None), (300, 512, 512, 8, 4, 2.0),
                                             (200, 1024, 256, 16, 8, None), (700, 256, 768, 8, 2, 6.0),
                                             (5, 8192, 256, 4, 2, None), (200, 1024, 512, 16, 8, None),
-                                            (700, 512, 1536, 8, 2, 6.0), (150, 6144, 512, 8, 4, 1.5)])
+                                            (700, 512, 1536, 8, 2, 6.0), (150, 6144, 512, 8, 4, 1.5),
+                                            # expert counts that are not a multiple of 64
+                                            (70, 256, 128, 65, 4, None), (20, 512, 256, 200, 8, 2.0)])
 def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew, packed):
     log("gemm1 lossless T=%d H=%d I=%d E=%d k=%d packed=%s" % (T, H, I, E, k, packed))
     N = T * k
@@ -239,7 +241,8 @@ def test_gemm1_preact_lossless_bitexact(moe, T, H, I, E, k, skew, packed):
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("T,H,I,E,k", [(64, 256, 128, 8, 2), (40, 512, 256, 16, 4), (9, 4096, 2048, 8, 8),
                                        (33, 384, 640, 5, 2), (300, 512, 512, 8, 4), (200, 1280, 256, 16, 8),
-                                       (50, 384, 512, 6, 2), (200, 1536, 1024, 16, 8), (150, 6144, 512, 8, 4)])
+                                       (50, 384, 512, 6, 2), (200, 1536, 1024, 16, 8), (150, 6144, 512, 8, 4),
+                                       (70, 256, 128, 65, 4), (20, 512, 256, 200, 8)])
 def test_gemm2_lossless_bitexact(moe, T, H, I, E, k, packed):
     log("gemm2 lossless T=%d H=%d I=%d E=%d k=%d packed=%s" % (T, H, I, E, k, packed))
     N = T * k
@@ -251,6 +254,45 @@ def test_gemm2_lossless_bitexact(moe, T, H, I, E, k, packed):
     W = moe.ExpertWeights(dev(w13), dev(w13_s), dev(w2), dev(w2_s))
     if packed:
         W = moe.prepack_weights(p, W)
+    y = torch.full((N, H), float("nan"), dtype=torch.float32, device="cuda")
+    moe.grouped_gemm2(p, dev(hq), dev(hs), dev(off), W, y, ws)
+    torch.cuda.synchronize()
+    Hd = F.dequantize_fp8_blocks(hq, hs)
+    ref = np.zeros((N, H))
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            ref[r0:r1] = Hd[r0:r1] @ F.decode_mxfp4(w2[e], w2_s[e]).T
+    assert np.array_equal(host(y).astype(np.float64), ref)
+
+
+# Expert offsets handed in directly (the staged entry points take any
+# non-decreasing offsets): every row in the first or in the last expert, rows
+# only in the odd experts, rows dealt one by one over all experts.  The
+# streaming kernels find each m-tile from these offsets alone.
+@pytest.mark.parametrize("pattern", ["first", "last", "alternate", "dealt"])
+@pytest.mark.parametrize("E", [130, 512])
+def test_gemm2_lossless_given_offsets(moe, pattern, E):
+    T, H, I, k = 40, 256, 128, 4
+    N = T * k
+    log("gemm2 lossless given offsets %s E=%d" % (pattern, E))
+    counts = np.zeros(E, dtype=np.int64)
+    if pattern == "first":
+        counts[0] = N
+    elif pattern == "last":
+        counts[E - 1] = N
+    elif pattern == "alternate":
+        odd = np.arange(1, E, 2)
+        np.add.at(counts, odd[np.arange(N) % len(odd)], 1)
+    else:
+        np.add.at(counts, np.arange(N) % E, 1)   # dealt
+    assert counts.sum() == N
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    hq, hs, w2, w2_s = S.lossless_gemm_inputs(N, I, H, seed=5, batch=E)
+    _, _, w13, w13_s = S.lossless_gemm_inputs(1, H, 2 * I, seed=6, batch=E)
+    p = moe.Problem.make(T, H, I, E, k)
+    ws = moe.alloc_workspace(p)
+    W = moe.prepack_weights(p, moe.ExpertWeights(dev(w13), dev(w13_s), dev(w2), dev(w2_s)))
     y = torch.full((N, H), float("nan"), dtype=torch.float32, device="cuda")
     moe.grouped_gemm2(p, dev(hq), dev(hs), dev(off), W, y, ws)
     torch.cuda.synchronize()
