@@ -169,13 +169,18 @@ FULL = [("tiny", True), ("flash_decode", True), ("pro_decode", True), ("flash_pr
         # FP8 block-scaled experts
         ("flash_decode_fp8", True), ("flash_decode_fp8", False), ("pro_decode_fp8", True),
         ("flash_prefill_fp8", True)]
+# sigmoid scoring at full size: zero bias (Flash decode) and the Zipf
+# selection bias (Pro skewed prefill)
+FULL_SIGMOID = [("flash_decode", True), ("pro_skewed_prefill", True)]
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg,packed", FULL)
-def test_forward_full_size_sampled(moe, cfg, packed):
-    log("full-size %s packed=%s: generating layer" % (cfg, packed))
+@pytest.mark.parametrize("cfg,packed,score", [(c, pk, "softmax") for c, pk in FULL] +
+                         [pytest.param(c, pk, "sigmoid", id="sigmoid-%s" % c) for c, pk in FULL_SIGMOID])
+def test_forward_full_size_sampled(moe, cfg, packed, score):
+    log("full-size %s packed=%s score=%s: generating layer" % (cfg, packed, score))
     lay = S.make_layer(cfg, seed=0)
+    lay["score"] = score
     p = problem(lay)
     T, H = lay["x"].shape
     E, k = p.num_experts, p.top_k
@@ -201,8 +206,8 @@ def test_forward_full_size_sampled(moe, cfg, packed):
     tol = logit_tol(ref["logits"])
     Lg = Lall[toks].astype(np.float64)
     assert np.all(np.abs(Lg - ref["logits"]) <= tol)
-    margin = key_margin(Lg, ref["logits"], b)
-    clear = unambiguous_tokens(ref["logits"], k, b, margin, order=False)
+    margin = key_margin(Lg, ref["logits"], b, score)
+    clear = unambiguous_tokens(ref["logits"], k, b, margin, order=False, score=score)
     assert np.array_equal(np.sort(ids_g[toks][clear], 1), np.sort(ref["ids"][clear], 1))
     assert clear.any()
     err, share = check_output(y[toks], ref, rows=clear)
