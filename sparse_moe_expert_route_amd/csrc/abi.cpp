@@ -56,7 +56,7 @@ Layout layout_of(const moe_problem& p) {
     L.block_counts = take(nblk * E * 4);
     L.block_base = take(nblk * E * 4);
     L.tile_start = take((E + 1) * 4);
-    L.tile_info = take((size_t)max_tiles((int64_t)N, (int)E, kRowsPerTile) * 16);   // bound for both tile sizes
+    L.tile_info = take((size_t)max_tiles((int64_t)N, (int)E, kRowsPerTile) * 16);   // a bound for any tile size
     const size_t sb = scale_bytes(p);
     L.xq = take(N * H);
     L.xs = take(N * (H / kFp8Block) * sb);
@@ -118,18 +118,19 @@ moe_status run_route(const moe_problem& p, const void* x, const void* wr, const 
 bool use_tiled(const moe_problem& p);
 
 // Permutation and FP8 gather.  Up to kPermBlock slots (decode) one workgroup
-// does the whole permutation and also writes the GEMMs' tile plan into the
-// workspace; *planned tells the caller that it may skip the plan.
+// does the whole permutation and, when the tiled GEMMs will run, also writes
+// their tile plan into the workspace (the streaming GEMMs need none);
+// *planned tells the caller that it may skip the plan.
 moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, int32_t* offsets,
                        int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, void* xs, void* ws,
                        hipStream_t stream, bool* planned = nullptr, bool fuse_gather = false) {
     const Layout L = layout_of(p);
     const int64_t N = p.num_tokens * p.top_k;
     if (N <= kPermBlock) {
-        const int rpt = use_tiled(p) ? kRowsPerTileTiled : kRowsPerTile;
+        const int plan_tiles = use_tiled(p) ? max_tiles(N, p.num_experts, kRowsPerTileTiled) : 0;
         MOE_LAUNCH(launch_perm_small(ids, offsets, sorted_token, row_of_slot, at<int32_t>(ws, L.tile_start),
-                                     at<int4>(ws, L.tile_info), N, p.num_experts, p.top_k, rpt,
-                                     max_tiles(N, p.num_experts, rpt), stream));
+                                     at<int4>(ws, L.tile_info), N, p.num_experts, p.top_k, kRowsPerTileTiled,
+                                     plan_tiles, stream));
         if (planned) *planned = true;
     } else {
         int32_t* bc = at<int32_t>(ws, L.block_counts);

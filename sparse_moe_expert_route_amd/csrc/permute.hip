@@ -101,9 +101,10 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------
 // All of the permutation for at most kPermBlock slots (decode), plus the
-// grouped GEMMs' tile plan, in one workgroup: expert histogram, the two
+// tiled GEMMs' tile plan, in one workgroup: expert histogram, the two
 // exclusive scans (rows and m-tiles), the stable in-block rank of every slot
-// (the ballot match of perm_scatter_kernel) and the per-tile descriptors.
+// (the ballot match of perm_scatter_kernel) and the per-tile descriptors
+// (max_tiles of them; 0 when the streaming GEMMs run, which need none).
 // One launch instead of four.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* __restrict__ ids,
