@@ -268,13 +268,44 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        unsigned long long o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+// Largest value over the wave, returned wave-uniform: DPP shifts by 1, 2, 4
+// and 8 lanes leave each 16-lane row's maximum in its lane 15, two row
+// broadcasts (row 0 into row 1 and row 2 into row 3, then lane 31 into rows 2
+// and 3) carry the maxima to lane 63, and a readlane returns it.  DPP moves
+// stay in the VALU; a shuffle goes through LDS and costs far more latency.
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v, uint32_t t) { return t > v ? t : v; }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xf, 0xf, false));   // row_shr:1
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xf, 0xf, false));   // row_shr:2
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xf, 0xf, false));   // row_shr:4
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xf, 0xf, false));   // row_shr:8
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));   // row_bcast:15
+    v = dpp_max_step(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));   // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// The same pattern for a float maximum and a float sum (lanes without a DPP
+// source add 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+    v = fmaxf(v, dpp_f<0x111, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x112, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x114, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x118, 0xf>(v, v));
+    v = fmaxf(v, dpp_f<0x142, 0xa>(v, v));
+    v = fmaxf(v, dpp_f<0x143, 0xc>(v, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+    v += dpp_f<0x111, 0xf>(0.0f, v);
+    v += dpp_f<0x112, 0xf>(0.0f, v);
+    v += dpp_f<0x114, 0xf>(0.0f, v);
+    v += dpp_f<0x118, 0xf>(0.0f, v);
+    v += dpp_f<0x142, 0xa>(0.0f, v);
+    v += dpp_f<0x143, 0xc>(0.0f, v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // SIG: sigmoid scoring (teardown "How Big Is Each Expert?": sigmoid expert
@@ -314,8 +345,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         unsigned long long best = 0;
 #pragma unroll
         for (int q = 0; q < EJ; ++q) best = key[q] > best ? key[q] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
+        // the largest ordered key, then among the lanes holding it the
+        // largest ~id (the lowest expert id)
+        const uint32_t hi = wave_max_u32((uint32_t)(best >> 32));
+        const uint32_t lo = wave_max_u32((uint32_t)(best >> 32) == hi ? (uint32_t)best : 0u);
+        const int e = (int)(~lo);
         const int owner = e & 63, slot = e >> 6;
         float lsel = 0.0f;
         if (lane == owner) {
@@ -323,7 +357,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
             for (int q = 0; q < EJ; ++q)
                 if (q == slot) { key[q] = 0; lsel = lv[q]; }
         }
-        lsel = __shfl(lsel, owner, 64);
+        lsel = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsel), owner));
         if (lane == j) { sel = lsel; sid = e; }
     }
 
@@ -333,14 +367,10 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     if constexpr (SIG) {
         z = lane < k ? sel : 0.0f;
     } else {
-        float m = lane < k ? sel : -__builtin_inff();
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        const float m = wave_max_f32(lane < k ? sel : -__builtin_inff());
         z = lane < k ? expf(sel - m) : 0.0f;
     }
-    float s = z;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+    const float s = wave_sum_f32(z);
     if (lane < k) {
         ids[(size_t)t * k + lane] = sid;
         w[(size_t)t * k + lane] = z / s;
