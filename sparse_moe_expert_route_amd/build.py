@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["abi.cpp", "router.hip", "permute.hip", "prepack.hip", "expert_gemm.hip", "expert_gemm_tiled.hip", "expert_gemm_fp8.hip", "expert_gemm_fp8_tiled.hip", "combine.hip"]
-HEADERS = ["moe_internal.h"]
+HEADERS = ["moe_internal.h", "fp8_rows.h"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

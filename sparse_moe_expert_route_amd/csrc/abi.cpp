@@ -106,10 +106,19 @@ bool all_aligned(P p, R... rest) { return p && aligned16(p) && all_aligned(rest.
 
 // ---- launch sequences (arguments already validated) ----------------------
 
+// With xq/xs given and a decode-sized batch, the router launch also writes the
+// token-order FP8 copy of x; *quantised tells the caller.
 moe_status run_route(const moe_problem& p, const void* x, const void* wr, const float* bias, float* logits,
-                     int32_t* ids, float* w, hipStream_t stream) {
-    if (x) MOE_LAUNCH(launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, logits, p.num_tokens, p.hidden,
-                                           p.num_experts, stream));
+                     int32_t* ids, float* w, hipStream_t stream, uint8_t* xq = nullptr, void* xs = nullptr,
+                     bool* quantised = nullptr) {
+    const bool with_quant = x && xq && p.num_tokens <= kDecodeRouterMaxT;
+    if (quantised) *quantised = with_quant;
+    if (with_quant)
+        MOE_LAUNCH(launch_router_quant((const uint16_t*)x, (const uint16_t*)wr, logits, p.num_tokens, p.hidden,
+                                       p.num_experts, xq, xs, fp8_block(p), stream));
+    else if (x)
+        MOE_LAUNCH(launch_router_logits((const uint16_t*)x, (const uint16_t*)wr, logits, p.num_tokens, p.hidden,
+                                        p.num_experts, stream));
     MOE_LAUNCH(launch_topk(logits, bias, ids, w, p.num_tokens, p.num_experts, p.top_k,
                            p.score_func == MOE_SCORE_SIGMOID_BIAS, stream));
     return MOE_OK;
@@ -123,7 +132,8 @@ bool use_tiled(const moe_problem& p);
 // *planned tells the caller that it may skip the plan.
 moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, int32_t* offsets,
                        int32_t* sorted_token, int32_t* row_of_slot, uint8_t* xq, void* xs, void* ws,
-                       hipStream_t stream, bool* planned = nullptr, bool fuse_gather = false) {
+                       hipStream_t stream, bool* planned = nullptr, bool fuse_gather = false,
+                       bool x_quantised = false) {
     const Layout L = layout_of(p);
     const int64_t N = p.num_tokens * p.top_k;
     if (N <= kPermBlock) {
@@ -141,13 +151,16 @@ moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, 
                                        stream));
         if (planned) *planned = false;
     }
-    // fused gather: quantise the T tokens once; GEMM-1 reads them through sorted_token
-    if (fuse_gather)
-        MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, nullptr, xq, xs, p.num_tokens, p.hidden, p.num_tokens,
-                                       fp8_block(p), stream));
-    else
+    // fused gather: quantise the T tokens once (unless the router launch already
+    // did); GEMM-1 reads them through sorted_token
+    if (fuse_gather) {
+        if (!x_quantised)
+            MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, nullptr, xq, xs, p.num_tokens, p.hidden, p.num_tokens,
+                                           fp8_block(p), stream));
+    } else {
         MOE_LAUNCH(launch_quant_gather((const uint16_t*)x, sorted_token, xq, xs, N, p.hidden, p.num_tokens,
                                        fp8_block(p), stream));
+    }
     return MOE_OK;
 }
 
@@ -385,11 +398,13 @@ moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_r
     uint8_t* hq = at<uint8_t>(ws, L.hq);
     void* hs = at<uint8_t>(ws, L.hs);
     float* y_perm = at<float>(ws, L.y_perm);
-    MOE_CHECK(run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, ids, w, stream));
     // the FP8 gather is fused into GEMM-1: x is quantised once per token (T rows
-    // instead of T*k) and GEMM-1 reads its rows through sorted_token
+    // instead of T*k; on decode batches in the router's launch) and GEMM-1 reads
+    // its rows through sorted_token
+    bool quantised = false;
+    MOE_CHECK(run_route(*p, x_bf16, w_router_bf16, sel_bias, logits, ids, w, stream, xq, xs, &quantised));
     bool planned = false;
-    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream, &planned, true));
+    MOE_CHECK(run_permute(*p, ids, x_bf16, offsets, st, ros, xq, xs, ws, stream, &planned, true, quantised));
     MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq, xs, offsets, *weights, hq, hs, ws, !planned, stream, st));
     MOE_CHECK(run_gemm2(*p, hq, hs, offsets, *weights, y_perm, ws, false, stream));
     MOE_LAUNCH(launch_combine(y_perm, ros, w, y, out_dtype == MOE_OUT_BF16, p->num_tokens, p->hidden, p->top_k,

@@ -81,6 +81,12 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, flo
                                 int64_t T, int H, int E, hipStream_t stream);
 hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, int64_t T, int E,
                        int k, int sigmoid, hipStream_t stream);
+// Up to kDecodeRouterMaxT tokens the router runs its decode kernel; there it
+// can also write the token-order FP8 copy of x (xq [T][H], xs [T][H/128]) in
+// the same launch.
+constexpr int kDecodeRouterMaxT = 256;
+hipError_t launch_router_quant(const uint16_t* x, const uint16_t* w_router, float* logits, int64_t T, int H, int E,
+                               uint8_t* xq, void* xs, int f32_scales, hipStream_t stream);
 
 hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
                              hipStream_t stream);

@@ -4,6 +4,7 @@
 // "Router") and picks 8 experts per token ("How Big Is Each Expert?"), both
 // on the teardown page.
 #include "moe_internal.h"
+#include "fp8_rows.h"
 
 #include <type_traits>
 
@@ -21,18 +22,17 @@ namespace moe {
 // through LDS (decode shapes: few tokens, so split K for parallelism).
 // ---------------------------------------------------------------------------
 template <int TT, int KS>
-__global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ x,
-                                                             const uint16_t* __restrict__ wr,
-                                                             float* __restrict__ logits,
-                                                             int T, int H, int E) {
+__device__ __forceinline__ void router_logits_block(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+                                                    float* __restrict__ logits, int T, int H, int E, int bx,
+                                                    int by) {
     constexpr int kGroups = 4 / KS;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int ks = wave % KS;
     const int eg = wave / KS;
     const int g = lane >> 4, r = lane & 15;
-    const int e0 = (blockIdx.x * kGroups + eg) * 16;
-    const int t0 = blockIdx.y * (16 * TT);
+    const int e0 = (bx * kGroups + eg) * 16;
+    const int t0 = by * (16 * TT);
 
     const int erow = min(e0 + r, E - 1);
     const uint16_t* wp = wr + (size_t)erow * H;
@@ -105,6 +105,32 @@ __global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __re
                 if (e + i < E) o[i] = acc[j][i];
         }
     }
+}
+
+template <int TT, int KS>
+__global__ void __launch_bounds__(256) router_logits_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wr,
+                                                             float* __restrict__ logits,
+                                                             int T, int H, int E) {
+    router_logits_block<TT, KS>(x, wr, logits, T, H, E, blockIdx.x, blockIdx.y);
+}
+
+// Decode forward: the router logits and the token-order FP8 copy of x in one
+// launch.  Block rows y < gy compute logits as router_logits_kernel does; the
+// rows after them quantise token rows, one per workgroup.  The two parts
+// share nothing, so no workgroup waits for another.
+template <bool F32S>
+__global__ void __launch_bounds__(256) router_quant_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wr,
+                                                           float* __restrict__ logits, int T, int H, int E,
+                                                           int gy, uint8_t* __restrict__ xq,
+                                                           void* __restrict__ xs) {
+    if ((int)blockIdx.y < gy) {
+        router_logits_block<1, 4>(x, wr, logits, T, H, E, blockIdx.x, blockIdx.y);
+        return;
+    }
+    const int r = ((int)blockIdx.y - gy) * (int)gridDim.x + (int)blockIdx.x;
+    if (r < T) quantise_row<F32S>(x + (size_t)r * H, xq, xs, r, H);
 }
 
 // ---------------------------------------------------------------------------
@@ -237,9 +263,24 @@ __global__ void __launch_bounds__(256) router_logits_tiled_kernel(const uint16_t
     }
 }
 
+hipError_t launch_router_quant(const uint16_t* x, const uint16_t* w_router, float* logits, int64_t T, int H, int E,
+                               uint8_t* xq, void* xs, int f32_scales, hipStream_t stream) {
+    if (T > kDecodeRouterMaxT) return hipErrorInvalidValue;
+    const int gx = (E + 15) / 16, gy = (int)((T + 15) / 16);
+    const int gq = (int)((T + gx - 1) / gx);   // token rows to quantise, gx per block row
+    dim3 grid(gx, gy + gq);
+    if (f32_scales)
+        hipLaunchKernelGGL(router_quant_kernel<true>, grid, dim3(256), 0, stream, x, w_router, logits, (int)T, H, E,
+                           gy, xq, xs);
+    else
+        hipLaunchKernelGGL(router_quant_kernel<false>, grid, dim3(256), 0, stream, x, w_router, logits, (int)T, H, E,
+                           gy, xq, xs);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, float* logits,
                                 int64_t T, int H, int E, hipStream_t stream) {
-    if (T <= 256) {
+    if (T <= kDecodeRouterMaxT) {
         // decode shapes: 16 tokens x 16 experts per workgroup, K split over 4 waves
         dim3 grid((E + 15) / 16, (unsigned)((T + 15) / 16));
         hipLaunchKernelGGL((router_logits_kernel<1, 4>), grid, dim3(256), 0, stream, x, w_router, logits,
