@@ -270,12 +270,14 @@ def test_gemm2_lossless_bitexact(moe, T, H, I, E, k, packed):
 # non-decreasing offsets): every row in the first or in the last expert, rows
 # only in the odd experts, rows dealt one by one over all experts.  The
 # streaming kernels find each m-tile from these offsets alone.
+# H = 1024, I = 512 runs the down GEMM with its scales staged in LDS.
 @pytest.mark.parametrize("pattern", ["first", "last", "alternate", "dealt"])
 @pytest.mark.parametrize("E", [130, 512])
-def test_gemm2_lossless_given_offsets(moe, pattern, E):
-    T, H, I, k = 40, 256, 128, 4
+@pytest.mark.parametrize("H,I", [(256, 128), (1024, 512)])
+def test_gemm2_lossless_given_offsets(moe, pattern, E, H, I):
+    T, k = 40, 4
     N = T * k
-    log("gemm2 lossless given offsets %s E=%d" % (pattern, E))
+    log("gemm2 lossless given offsets %s E=%d H=%d I=%d" % (pattern, E, H, I))
     counts = np.zeros(E, dtype=np.int64)
     if pattern == "first":
         counts[0] = N
