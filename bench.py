@@ -6,19 +6,23 @@ GEMM, weighted combine) through moe_forward, on one synthetic batch already
 resident in HBM.
 
 Prints ONE JSON line:
-  value        tokens/s of the whole layer (T tokens per step / wall time per step)
+  value        tokens/s of the whole layer: T tokens / the median step time, each
+               step timed alone with HIP events around moe_forward after a 1 GiB
+               write that evicts the L2s and the 256 MB last-level cache (the
+               timed loop is exactly `steps` such steps, bracketed by device
+               synchronisations); `warm` is the rate of `steps` back-to-back
+               steps with no flush
   roofline     the dominant kernel (the gate/up expert GEMM), timed with HIP
                events on the stream it runs on: algorithmic bytes (below the
                625 FLOP/byte ridge point: HBM-bound) or FLOPs (above it:
                MFMA-bound) per launch / mean launch duration, against the
                MI355X peak; traffic = HBM bytes per launch from the counter
                summaries in profiles/ while the GEMM sources are unchanged
-  cold_cache_step  per-step HIP-event times of moe_forward with a 1 GiB cache
-               flush before each step (median, p10, p90)
+  cold_cache_step  the per-step HIP-event times behind `value` (median, p10, p90)
   graph_replay the same step captured once as a HIP graph and replayed
   cpu_baseline the CPU oracle on a bounded sample of the same workload
-Workloads: tiny, flash_decode (default), flash_prefill, pro_decode,
-pro_skewed_prefill, their one-GPU tensor-parallel shares (*_tp4), the
+Workloads: tiny, flash_decode, flash_prefill, pro_decode,
+pro_skewed_prefill (default: the largest), their one-GPU tensor-parallel shares (*_tp4), the
 speculative-verify blocks flash_verify, pro_verify, and the FP8 block-scaled
 expert format (*_fp8: e4m3 weights, float32 128 x 128 block scales) (see
 synthetic/__init__.py).
@@ -47,12 +51,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="flash_decode")
+    ap.add_argument("--config", default="pro_skewed_prefill")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-flush", action="store_true",
-                    help="skip the cold-cache per-step timing (1 GiB cache flush before each step)")
+                    help="time the steps without the 1 GiB cache flush before each (value = warm rate)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens for the CPU oracle (0 = auto)")
     ap.add_argument("--canonical-weights", action="store_true",
                     help="run on the canonical (row-major) weight layout instead of the packed one")
@@ -146,7 +150,7 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # ---- whole layer: warmup, then exactly `steps` timed steps ----
+    # ---- whole layer, warm: warmup, then `steps` back-to-back steps ----
     for _ in range(args.warmup):
         moe.forward(p, x, wr, bias, W, y, ws)
     torch.cuda.synchronize()
@@ -154,31 +158,38 @@ def main():
     for _ in range(args.steps):
         moe.forward(p, x, wr, bias, W, y, ws)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall / args.steps * 1e3
-    tokens_per_s = T * args.steps / wall
-    log("bench: %.3f ms/step, %.0f tokens/s" % (ms_per_step, tokens_per_s))
+    warm_wall = time.perf_counter() - t0
+    warm = {"ms_per_step": round(warm_wall / args.steps * 1e3, 4), "value": round(T * args.steps / warm_wall, 1)}
+    log("bench: warm %.3f ms/step, %.0f tokens/s" % (warm["ms_per_step"], warm["value"]))
 
-    # ---- per-step times with cold caches: before each step a 1 GiB write evicts the
-    # L2s and the 256 MB last-level cache, then HIP events bracket moe_forward alone ----
+    # ---- the timed loop: exactly `steps` steps with cold caches.  Before each step a
+    # 1 GiB write evicts the L2s and the 256 MB last-level cache, then HIP events on the
+    # launching stream bracket moe_forward alone; value = T / median step time ----
     flushed = None
-    if not args.no_flush:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        stream = torch.cuda.current_stream()
-        times = []
-        for _ in range(args.steps):
+    scratch = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        if scratch is not None:
             scratch.fill_(1.0)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            moe.forward(p, x, wr, bias, W, y, ws)
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        del scratch
-        q = np.percentile(np.array(times), [10, 50, 90])
-        flushed = {"ms_p10": round(float(q[0]), 4), "ms_median": round(float(q[1]), 4),
-                   "ms_p90": round(float(q[2]), 4), "value_median": round(T / (float(q[1]) * 1e-3), 1)}
-        log("bench: cold-cache step median %.3f ms (p10 %.3f, p90 %.3f)" % (q[1], q[0], q[2]))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        moe.forward(p, x, wr, bias, W, y, ws)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    torch.cuda.synchronize()
+    loop_wall = time.perf_counter() - t0
+    del scratch
+    q = np.percentile(np.array(times), [10, 50, 90])
+    ms_per_step = float(q[1])
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    flushed = {"ms_p10": round(float(q[0]), 4), "ms_median": round(float(q[1]), 4), "ms_p90": round(float(q[2]), 4),
+               "flush": not args.no_flush, "loop_wall_ms_per_step": round(loop_wall / args.steps * 1e3, 4)}
+    log("bench: %s step median %.3f ms (p10 %.3f, p90 %.3f), %.0f tokens/s"
+        % ("cold-cache" if not args.no_flush else "event-timed", q[1], q[0], q[2], tokens_per_s))
 
     # ---- the same step captured once as a HIP graph and replayed (no launch overhead) ----
     graph = None
@@ -281,6 +292,7 @@ def main():
            "config": {"workload": args.config, "T": T, "H": H, "E": E, "k": k, "I": inter, "seed": args.seed,
                       "bias": cfg["bias"], "experts": cfg["format"]},
            "roofline": roof, "layer": layer,
+           "warm": warm,
            "graph_replay": graph,
            "cold_cache_step": flushed,
            "weight_layout": "canonical" if args.canonical_weights else "packed",
@@ -291,30 +303,49 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(lay, args, T):
-    """The oracle, as it stands, on a bounded sample of tokens of the same workload (single thread)."""
-    import numpy as np
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:   # pragma: no cover
-        threadpool_limits = None
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(lay, args, T):
+    """The oracle, as it stands, on a bounded sample of tokens of the same workload, with
+    BLAS on every core this process may run on."""
+    import numpy as np
     from oracle import layer as OL
-    n = args.cpu_sample_tokens or (32 if T <= 256 else 8)
+    cores = len(os.sched_getaffinity(0))
+    n = args.cpu_sample_tokens or 8
     n = min(n, T)
     toks = np.arange(n)
-    log("bench: CPU oracle on %d tokens" % n)
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    blas = {"vendor": None, "threads": None}
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:   # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    log("bench: CPU oracle on %d tokens, %d cores" % (n, cores))
     t0 = time.perf_counter()
-    if ctx:
-        with ctx:
+    if threadpool_limits:
+        with threadpool_limits(limits=cores, user_api="blas"):
+            info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+            if info:
+                blas = {"vendor": "%s %s" % (info[0].get("internal_api"), info[0].get("version")),
+                        "threads": info[0].get("num_threads")}
             OL.forward_tokens(lay, toks)
     else:
         OL.forward_tokens(lay, toks)
     sec = time.perf_counter() - t0
-    return {"value": round(n / sec, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(n / sec, 4), "unit": "tokens/s", "cores": blas["threads"] or cores, "kind": "oracle",
+            "cpu": _cpu_model(), "blas": blas["vendor"], "affinity_cores": cores,
             "sample": "first %d tokens of the %s workload, whole layer (router, routing, FP8 quantisation, all "
-                      "their experts decoded from %s and run in float64, combine); %.1f s"
-                      % (n, args.config, "FP8 blocks" if lay.get("format") == "fp8_block" else "MXFP4", sec)}
+                      "their experts decoded from %s and run in float64 with BLAS on %s threads, combine); %.1f s"
+                      % (n, args.config, "FP8 blocks" if lay.get("format") == "fp8_block" else "MXFP4",
+                         blas["threads"] or cores, sec)}
 
 
 if __name__ == "__main__":

@@ -30,6 +30,10 @@
  *     as a status; nothing is launched then.  A failed launch returns
  *     MOE_ERR_HIP.  num_tokens == 0 returns MOE_OK and launches nothing.
  *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ *   - Data errors that only the device can see (expert ids, expert offsets)
+ *     are reported in two device error words in the workspace (see
+ *     moe_error_words_offset); the kernels clamp every access such an error
+ *     would send out of bounds, and the affected results are unspecified.
  *   - Pointers must be 16-byte aligned.
  *   - Limits: hidden and intermediate multiples of 128, 1 <= num_experts
  *     <= 512, 1 <= top_k <= min(num_experts, 8), num_tokens * top_k < 2^31.
@@ -47,7 +51,7 @@ extern "C" {
 /* Same declaration as the HIP runtime's: a stream handle is an opaque pointer. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
     MOE_OK = 0,
@@ -60,7 +64,8 @@ typedef enum {
 /* How experts are scored, selected and weighted (b = optional selection bias).
  * MOE_SCORE_SOFTMAX_TOPK: key = L + b (fp32 add); weights = softmax over the
  *   k selected logits L (the measured workloads).
- * MOE_SCORE_SIGMOID_BIAS: s = sigmoid(L) = 1 / (1 + e^-L) in fp32;
+ * MOE_SCORE_SIGMOID_BIAS: s = sigmoid(L) = 1 / (1 + e^-L), evaluated in
+ *   float64 and rounded once to fp32;
  *   key = s + b (fp32 add); weights = the k selected s divided by their sum
  *   (teardown "How Big Is Each Expert?": sigmoid expert scores, plus a
  *   per-expert bias that balances the load across experts).
@@ -125,6 +130,14 @@ typedef struct {
  *   Same bytes, reordered so that one 64-lane load covers whole cache lines. */
 typedef enum { MOE_WEIGHTS_CANONICAL = 0, MOE_WEIGHTS_PACKED = 1 } moe_weight_layout;
 
+/* Bits of the device error words (moe_error_words_offset).                */
+typedef enum {
+    MOE_DEVERR_EXPERT_ID_RANGE = 1,      /* a topk_ids entry outside [0, E)          */
+    MOE_DEVERR_EXPERT_ID_DUPLICATE = 2,  /* one expert id twice among a token's k     */
+    MOE_DEVERR_EXPERT_OFFSETS = 4        /* expert_offsets not 0 = o[0] <= o[1] <= ...
+                                            <= o[E] = T*k                           */
+} moe_device_error;
+
 typedef struct {
     const uint8_t* w13;
     const uint8_t* w13_scale;
@@ -142,6 +155,21 @@ const char* moe_status_string(moe_status status);
 /* Workspace bytes every entry point of this header needs for `problem`
  * (the maximum over entry points).  Returns 0 for an invalid problem. */
 size_t moe_workspace_size(const moe_problem* problem);
+
+/* Byte offset, inside the workspace, of two uint32 device error words
+ * (bits: moe_device_error; 0 = no error).  Each is overwritten, in stream
+ * order, by the kernels of every call that checks it, so it describes the
+ * latest such call on that workspace; read it after that call's stream work
+ * has finished (for instance with a device-to-host copy on the same stream).
+ *   word 0  moe_permute and moe_forward: the routed expert ids
+ *           (MOE_DEVERR_EXPERT_ID_RANGE, MOE_DEVERR_EXPERT_ID_DUPLICATE)
+ *   word 1  the grouped-GEMM entry points and moe_forward: the expert offsets
+ *           (MOE_DEVERR_EXPERT_OFFSETS); moe_permute writes 0 here when it
+ *           also builds the GEMMs' tile plan
+ * With an id out of range the slot gets row_of_slot -1 and no row; with
+ * invalid offsets the GEMMs write no output rows (LDS-tiled kernels) or only
+ * rows inside the clamped offsets (streaming kernels).                     */
+size_t moe_error_words_offset(void);
 
 /* Reorder the expert weights into MOE_WEIGHTS_PACKED (a permutation of
  * bytes, nothing is rounded).  Meant to run once, when weights are loaded.
@@ -229,7 +257,9 @@ moe_status moe_grouped_gemm2(const moe_problem* problem, const uint8_t* hq_perm,
 
 /* Weighted combine: y[t] = sum_{j=0..k-1} topk_w[t][j] * y_perm[row_of_slot[t*k+j]],
  * accumulated in fp32 in slot order; out_dtype MOE_OUT_BF16 stores the
- * round-to-nearest-even bf16 of that fp32 sum.
+ * round-to-nearest-even bf16 of that fp32 sum.  A slot whose row lies
+ * outside [0, T*k) (row -1: moe_permute's answer to an id out of range)
+ * contributes nothing and is not read.
  *   y [T][H] fp32 or bf16 out                                             */
 moe_status moe_combine(const moe_problem* problem, const float* y_perm, const int32_t* row_of_slot,
                        const float* topk_w, void* y, int32_t out_dtype, hipStream_t stream);

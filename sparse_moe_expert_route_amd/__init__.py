@@ -21,7 +21,7 @@ __all__ = [
     "alloc_workspace", "prepack_weights", "route", "permute", "grouped_gemm_swiglu", "grouped_gemm1_swiglu",
     "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "OUT_F32", "OUT_BF16",
     "WEIGHTS_CANONICAL", "WEIGHTS_PACKED", "EXPERTS_MXFP4", "EXPERTS_FP8_BLOCK", "EXPORTED_SYMBOLS",
-    "scale_dtype",
+    "scale_dtype", "error_words", "DEVERR_EXPERT_ID_RANGE", "DEVERR_EXPERT_ID_DUPLICATE", "DEVERR_EXPERT_OFFSETS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,9 +33,13 @@ WEIGHTS_CANONICAL = 0
 WEIGHTS_PACKED = 1
 EXPERTS_MXFP4 = 0
 EXPERTS_FP8_BLOCK = 1
+DEVERR_EXPERT_ID_RANGE = 1
+DEVERR_EXPERT_ID_DUPLICATE = 2
+DEVERR_EXPERT_OFFSETS = 4
 
 EXPORTED_SYMBOLS = [
-    "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_prepack_weights", "moe_route", "moe_permute",
+    "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_error_words_offset", "moe_prepack_weights",
+    "moe_route", "moe_permute",
     "moe_grouped_gemm_swiglu", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_preact",
     "moe_grouped_gemm2", "moe_combine", "moe_forward",
 ]
@@ -123,6 +127,8 @@ def load():
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_workspace_size.restype = sz
     L.moe_workspace_size.argtypes = [P]
+    L.moe_error_words_offset.restype = sz
+    L.moe_error_words_offset.argtypes = []
     L.moe_prepack_weights.argtypes = [P, W, vp, vp, vp, vp, vp]
     L.moe_route.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     L.moe_permute.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -133,7 +139,7 @@ def load():
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, i32, vp]
     L.moe_forward.argtypes = [P, vp, vp, vp, W, vp, i32, vp, sz, vp]
     for name in EXPORTED_SYMBOLS:
-        if name not in ("moe_abi_version", "moe_status_string", "moe_workspace_size"):
+        if name not in ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_error_words_offset"):
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -179,6 +185,18 @@ def workspace_size(p):
 
 def alloc_workspace(p, device="cuda"):
     return torch.empty(workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def error_words(ws, stream=None):
+    """The two device error words of a workspace, as Python ints (word 0: expert ids of the
+    latest permutation; word 1: expert offsets of the latest grouped GEMM).  Waits for the
+    stream's work so far."""
+    off = load().moe_error_words_offset()
+    s = torch.cuda.current_stream() if stream is None else stream
+    with torch.cuda.stream(s):
+        w = ws[off:off + 8].cpu()
+    v = w.view(torch.int32).tolist()
+    return v[0] & 0xFFFFFFFF, v[1] & 0xFFFFFFFF
 
 
 def prepack_weights(p, weights, w13_packed=None, w2_packed=None, w13_scale_packed=None, w2_scale_packed=None,

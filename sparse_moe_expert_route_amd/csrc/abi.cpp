@@ -14,12 +14,17 @@ using namespace moe;
 
 constexpr size_t kAlign = 256;
 
+static_assert(kErrExpertIdRange == MOE_DEVERR_EXPERT_ID_RANGE && kErrExpertIdDuplicate == MOE_DEVERR_EXPERT_ID_DUPLICATE &&
+                  kErrExpertOffsets == MOE_DEVERR_EXPERT_OFFSETS,
+              "device error bits of the kernels and of moe.h");
+
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-    size_t logits, ids, w, offsets, sorted_token, row_of_slot, block_counts, block_base, tile_start, tile_info;
+    size_t errors, logits, ids, w, offsets, sorted_token, row_of_slot, block_counts, block_base, block_err;
+    size_t tile_start, tile_info;
     size_t xq, xs, hq, hs, y_perm, total;
 };
 
@@ -47,6 +52,7 @@ Layout layout_of(const moe_problem& p) {
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes ? bytes : 1); return o; };
+    L.errors = take(2 * sizeof(uint32_t));   // first: moe_error_words_offset() is 0
     L.logits = take(T * E * 4);
     L.ids = take(N * 4);
     L.w = take(N * 4);
@@ -55,6 +61,7 @@ Layout layout_of(const moe_problem& p) {
     L.row_of_slot = take(N * 4);
     L.block_counts = take(nblk * E * 4);
     L.block_base = take(nblk * E * 4);
+    L.block_err = take(nblk * 4);
     L.tile_start = take((E + 1) * 4);
     L.tile_info = take((size_t)max_tiles((int64_t)N, (int)E, kRowsPerTile) * 16);   // a bound for any tile size
     const size_t sb = scale_bytes(p);
@@ -139,14 +146,15 @@ moe_status run_permute(const moe_problem& p, const int32_t* ids, const void* x, 
     if (N <= kPermBlock) {
         const int plan_tiles = use_tiled(p) ? max_tiles(N, p.num_experts, kRowsPerTileTiled) : 0;
         MOE_LAUNCH(launch_perm_small(ids, offsets, sorted_token, row_of_slot, at<int32_t>(ws, L.tile_start),
-                                     at<int4>(ws, L.tile_info), N, p.num_experts, p.top_k, kRowsPerTileTiled,
-                                     plan_tiles, stream));
+                                     at<int4>(ws, L.tile_info), at<uint32_t>(ws, L.errors), N, p.num_experts,
+                                     p.top_k, kRowsPerTileTiled, plan_tiles, stream));
         if (planned) *planned = true;
     } else {
         int32_t* bc = at<int32_t>(ws, L.block_counts);
         int32_t* bb = at<int32_t>(ws, L.block_base);
-        MOE_LAUNCH(launch_perm_count(ids, bc, N, p.num_experts, stream));
-        MOE_LAUNCH(launch_perm_scan(bc, bb, offsets, N, p.num_experts, stream));
+        uint32_t* be = at<uint32_t>(ws, L.block_err);
+        MOE_LAUNCH(launch_perm_count(ids, bc, be, N, p.num_experts, p.top_k, stream));
+        MOE_LAUNCH(launch_perm_scan(bc, bb, offsets, be, at<uint32_t>(ws, L.errors), N, p.num_experts, stream));
         MOE_LAUNCH(launch_perm_scatter(ids, bb, offsets, sorted_token, row_of_slot, N, p.num_experts, p.top_k,
                                        stream));
         if (planned) *planned = false;
@@ -172,6 +180,7 @@ GemmArgs gemm_args(const moe_problem& p, const uint8_t* act, const void* act_sca
     a.act_rows = nullptr;
     a.w = w; a.w_scale = w_scale; a.out = out; a.out_scale = (uint8_t*)out_scale;
     a.packed = 0;
+    a.err = nullptr;
     a.N = p.num_tokens * p.top_k;
     a.H = p.hidden; a.I = p.intermediate; a.E = p.num_experts;
     return a;
@@ -208,12 +217,15 @@ moe_status run_gemm1(const moe_problem& p, GemmMode mode, const uint8_t* xq, con
     // only the tiled kernels read a tile plan; the streaming ones find their
     // m-tile from the offsets
     const int rpt = kRowsPerTileTiled;
+    const int64_t N = p.num_tokens * p.top_k;
+    uint32_t* err1 = at<uint32_t>(ws, L.errors) + 1;
     if (plan && use_tiled(p))
-        MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
-                                    max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
+        MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, err1, p.num_experts, rpt, max_tiles(N, p.num_experts, rpt), N,
+                                    stream));
     GemmArgs a = gemm_args(p, xq, xs, offsets, ts, ti, wt.w13, wt.w13_scale, out, out_scale);
     a.packed = wt.layout == MOE_WEIGHTS_PACKED;
     a.act_rows = act_rows;
+    a.err = use_tiled(p) ? nullptr : err1;   // the streaming kernels check the offsets themselves
     return launch_gemm(p, mode, a, stream);
 }
 
@@ -225,11 +237,14 @@ moe_status run_gemm2(const moe_problem& p, const uint8_t* hq, const void* hs, co
     // only the tiled kernels read a tile plan; the streaming ones find their
     // m-tile from the offsets
     const int rpt = kRowsPerTileTiled;
+    const int64_t N = p.num_tokens * p.top_k;
+    uint32_t* err1 = at<uint32_t>(ws, L.errors) + 1;
     if (plan && use_tiled(p))
-        MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, p.num_experts, rpt,
-                                    max_tiles(p.num_tokens * p.top_k, p.num_experts, rpt), stream));
+        MOE_LAUNCH(launch_tile_plan(offsets, ts, ti, err1, p.num_experts, rpt, max_tiles(N, p.num_experts, rpt), N,
+                                    stream));
     GemmArgs a = gemm_args(p, hq, hs, offsets, ts, ti, wt.w2, wt.w2_scale, y_perm, nullptr);
     a.packed = wt.layout == MOE_WEIGHTS_PACKED;
+    a.err = use_tiled(p) ? nullptr : err1;
     return launch_gemm(p, kGemm2, a, stream);
 }
 
@@ -254,6 +269,8 @@ size_t moe_workspace_size(const moe_problem* p) {
     if (check_problem(p) != MOE_OK) return 0;
     return layout_of(*p).total;
 }
+
+size_t moe_error_words_offset(void) { return 0; }
 
 moe_status moe_prepack_weights(const moe_problem* p, const moe_expert_weights* weights, uint8_t* w13_packed,
                                uint8_t* w13_scale_packed, uint8_t* w2_packed, uint8_t* w2_scale_packed,

@@ -20,6 +20,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
         rows[j] = row_of_slot[(size_t)t * k + min(j, k - 1)];
         ws[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
     }
+    // a slot without a row (row -1: moe_permute was given an expert id out of
+    // range, which its error word reports), or with a row outside the T*k rows
+    // of y_perm, adds nothing and is not loaded
+    bool has[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) has[j] = (unsigned)rows[j] < (unsigned)(T * k);
     // workgroup (t, b) covers channels [1024 b, 1024 b + 1024): a decode step
     // with few tokens still spreads over the whole chip.  All eight loads are
     // issued before the first FMA (slots past k re-read slot k-1 with weight
@@ -30,7 +36,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
         v4f acc = {0.f, 0.f, 0.f, 0.f};
         v4f v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load((const v4f*)(y_perm + (size_t)rows[j] * H + c));
+        for (int j = 0; j < 8; ++j)
+            v[j] = has[j] ? __builtin_nontemporal_load((const v4f*)(y_perm + (size_t)rows[j] * H + c))
+                          : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             acc[0] = fmaf(ws[j], v[j][0], acc[0]);

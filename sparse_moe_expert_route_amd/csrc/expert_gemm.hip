@@ -209,7 +209,12 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     const int g = lane >> 4, r = lane & 15;
 
     // ---- m-tile: expert, first row, rows ----
-    const int4 ti = find_stream_tile(a.offsets, a.E, blockIdx.y);
+    // workgroup 0 reports whether the offsets are valid (error word 1)
+    if (a.err && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 64) {
+        const uint32_t bad = offsets_error(a.offsets, a.E, a.N);
+        if (threadIdx.x == 0) *a.err = bad;
+    }
+    const int4 ti = find_stream_tile(a.offsets, a.E, (int)a.N, blockIdx.y);
     if (ti.x < 0) return;   // past the last m-tile
     const int e = ti.x, row0 = ti.y, nrows = ti.z;
 

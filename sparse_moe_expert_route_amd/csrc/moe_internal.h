@@ -16,6 +16,14 @@ constexpr int kFp8Block = 128;   // channels per activation scale
 constexpr int kMxBlock = 32;     // weight elements per e8m0 scale
 constexpr int kPermBlock = 1024; // routing slots per block of the permutation kernels
 
+// Device error words (two uint32 at the start of the workspace; the values
+// are those of moe_device_error in moe.h).  Word 0 is written by every
+// permutation, word 1 by every grouped-GEMM call, each with a plain store of
+// the whole word (no clearing needed, no atomics on global memory).
+constexpr uint32_t kErrExpertIdRange = 1u;      // a routed id outside [0, E)
+constexpr uint32_t kErrExpertIdDuplicate = 2u;  // one id twice among a token's k slots
+constexpr uint32_t kErrExpertOffsets = 4u;      // offsets not 0 = o[0] <= ... <= o[E] = T*k
+
 // ---------------------------------------------------------------------------
 // FP8 block quantisation rule (shared by the activation quantiser and the
 // SwiGLU epilogue): scale 2^e with e the smallest integer such that
@@ -88,17 +96,20 @@ constexpr int kDecodeRouterMaxT = 256;
 hipError_t launch_router_quant(const uint16_t* x, const uint16_t* w_router, float* logits, int64_t T, int H, int E,
                                uint8_t* xq, void* xs, int f32_scales, hipStream_t stream);
 
-hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
-                             hipStream_t stream);
+// block_err [ceil(N / kPermBlock)]: error bits of each block of slots, reduced
+// by the scan into err_word (word 0)
+hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, uint32_t* block_err, int64_t N, int E,
+                             int k, hipStream_t stream);
 hipError_t launch_perm_scan(const int32_t* block_counts, int32_t* block_base, int32_t* offsets,
-                            int64_t N, int E, hipStream_t stream);
+                            const uint32_t* block_err, uint32_t* err_word, int64_t N, int E, hipStream_t stream);
 hipError_t launch_perm_scatter(const int32_t* ids, const int32_t* block_base, const int32_t* offsets,
                                int32_t* sorted_token, int32_t* row_of_slot, int64_t N, int E, int k,
                                hipStream_t stream);
-// count + scan + scatter + tile plan in one workgroup, for N <= kPermBlock
+// count + scan + scatter + tile plan in one workgroup, for N <= kPermBlock;
+// writes error word 0, and word 1 (= 0) when it writes a tile plan
 hipError_t launch_perm_small(const int32_t* ids, int32_t* offsets, int32_t* sorted_token, int32_t* row_of_slot,
-                             int32_t* tile_start, int4* tile_info, int64_t N, int E, int k, int rows_per_tile,
-                             int max_tiles, hipStream_t stream);
+                             int32_t* tile_start, int4* tile_info, uint32_t* err_words, int64_t N, int E, int k,
+                             int rows_per_tile, int max_tiles, hipStream_t stream);
 // xs: e8m0 bytes (power-of-two scales), or float32 when f32_scales is set
 hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, uint8_t* xq,
                                void* xs, int64_t N, int H, int64_t T, int f32_scales, hipStream_t stream);
@@ -111,8 +122,10 @@ hipError_t launch_prepack_scales(const uint8_t* src, uint8_t* dst, int64_t rows,
 
 // tile_info[t] = {expert, first row, rows} of m-tile t for t < max_tiles
 // (expert -1 past the last tile); max_tiles = ceil(N / rows_per_tile) + E.
-hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, int E, int rows_per_tile,
-                            int max_tiles, hipStream_t stream);
+// Offsets that are not 0 = o[0] <= ... <= o[E] = N give an empty plan (no
+// tiles) and kErrExpertOffsets in *err_word (word 1); valid ones write 0.
+hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, uint32_t* err_word, int E,
+                            int rows_per_tile, int max_tiles, int64_t N, hipStream_t stream);
 inline int max_tiles(int64_t N, int E, int rows_per_tile) { return (int)((N + rows_per_tile - 1) / rows_per_tile) + E; }
 
 enum GemmMode { kGemm1Swiglu = 0, kGemm1Preact = 1, kGemm2 = 2 };
@@ -133,6 +146,7 @@ struct GemmArgs {
     const uint8_t* w_scale;    // e8m0 per 32 (float32 per 128 x 128 block for FP8 block-scaled experts)
     void* out;                 // swiglu: hq [N][I] + hs; preact: float [N][2I]; gemm2: float [N][H]
     uint8_t* out_scale;        // swiglu: hs [N][I/128] (e8m0, or float32 for FP8 block-scaled experts)
+    uint32_t* err;             // streaming kernels: error word 1 (offsets check), written by workgroup 0; or null
     int64_t N;
     int H, I, E;
     int packed;                // weight codes in the 16-row packed layout (moe_prepack_weights)
@@ -140,24 +154,37 @@ struct GemmArgs {
 constexpr int kRowsPerTile = 16;   // rows per m-tile of the streaming expert GEMM
 hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream);
 
+// Error bits of caller-given expert offsets (kErrExpertOffsets unless
+// 0 = o[0] <= o[1] <= ... <= o[E] = N), evaluated by one wave; every lane
+// returns the same value.
+__device__ __forceinline__ uint32_t offsets_error(const int32_t* __restrict__ offsets, int E, int64_t N) {
+    const int lane = threadIdx.x & 63;
+    bool bad = false;
+    for (int e = lane; e < E; e += 64) bad |= offsets[e] > offsets[e + 1];
+    if (lane == 0) bad |= offsets[0] != 0 || (int64_t)offsets[E] != N;
+    return __ballot(bad) ? kErrExpertOffsets : 0u;
+}
+
 // M-tile t of kRowsPerTile rows, looked up from the expert offsets alone
 // (expert e owns ceil(n_e / 16) tiles, in expert order), so the streaming
 // GEMMs need no tile plan.  One wave: lane l sums the tiles of its run of
 // ceil(E/64) <= 8 experts, a wave scan finds the lane whose run holds t, and
 // that lane's walk over its run gives the expert.  Every lane returns the
 // same {expert, first row, rows, 0}, expert -1 for t past the last tile.
-// Needs E <= 512.
-__device__ __forceinline__ int4 find_stream_tile(const int32_t* __restrict__ offsets, int E, int t) {
+// Offsets are clamped to [0, N] and a decreasing pair counts as an empty
+// expert, so invalid offsets (reported through offsets_error) still give
+// tiles inside the N rows.  Needs E <= 512.
+__device__ __forceinline__ int4 find_stream_tile(const int32_t* __restrict__ offsets, int E, int N, int t) {
     const int lane = threadIdx.x & 63;
     const int c = (E + 63) >> 6;
     const int e0 = min(lane * c, E), e1 = min(e0 + c, E);
     int o[9];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) o[i] = (e0 + i <= e1) ? offsets[e0 + i] : 0;
+    for (int i = 0; i < 9; ++i) o[i] = (e0 + i <= e1) ? min(max(offsets[e0 + i], 0), N) : 0;
     int n = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        if (e0 + i < e1) n += (o[i + 1] - o[i] + kRowsPerTile - 1) / kRowsPerTile;
+        if (e0 + i < e1) n += max(o[i + 1] - o[i] + kRowsPerTile - 1, 0) / kRowsPerTile;
     int incl = n;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -171,7 +198,7 @@ __device__ __forceinline__ int4 find_stream_tile(const int32_t* __restrict__ off
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if (e0 + i < e1) {
-            const int nt = (o[i + 1] - o[i] + kRowsPerTile - 1) / kRowsPerTile;
+            const int nt = max(o[i + 1] - o[i] + kRowsPerTile - 1, 0) / kRowsPerTile;
             if (t >= before && t < before + nt) {
                 e = e0 + i;
                 row0 = o[i] + (t - before) * kRowsPerTile;

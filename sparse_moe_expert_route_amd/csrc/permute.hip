@@ -10,22 +10,41 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// Error bits of slot s = t*k + j holding expert id `id`: out of range, or the
+// same id as an earlier slot of token t (the token's other ids are in the
+// same cache line or the next).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t slot_error(const int32_t* __restrict__ ids, int s, int id, int E, int k) {
+    if ((unsigned)id >= (unsigned)E) return kErrExpertIdRange;
+    const int j = s % k;
+    uint32_t err = 0;
+    for (int i = 1; i <= j; ++i) err |= ids[s - i] == id ? kErrExpertIdDuplicate : 0u;
+    return err;
+}
+
+// ---------------------------------------------------------------------------
 // Pass 1: per-block expert histogram of kPermBlock slots (LDS atomics only
-// count; they decide no position).
+// count; they decide no position), and the block's error bits.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) perm_count_kernel(const int32_t* __restrict__ ids,
                                                           int32_t* __restrict__ block_counts,
-                                                          int N, int E) {
+                                                          uint32_t* __restrict__ block_err,
+                                                          int N, int E, int k) {
     __shared__ int cnt[512];
+    __shared__ uint32_t err;
     for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+    if (threadIdx.x == 0) err = 0;
     __syncthreads();
     const int s = blockIdx.x * kPermBlock + threadIdx.x;
     if (s < N) {
         const int e = ids[s];
         if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // out-of-range ids are dropped
+        const uint32_t bad = slot_error(ids, s, e, E, k);
+        if (bad) atomicOr(&err, bad);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
+    if (threadIdx.x == 0) block_err[blockIdx.x] = err;
 }
 
 // ---------------------------------------------------------------------------
@@ -35,9 +54,18 @@ __global__ void __launch_bounds__(1024) perm_count_kernel(const int32_t* __restr
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(512) perm_scan_kernel(const int32_t* __restrict__ block_counts,
                                                         int32_t* __restrict__ block_base,
-                                                        int32_t* __restrict__ offsets, int nblk, int E) {
+                                                        int32_t* __restrict__ offsets,
+                                                        const uint32_t* __restrict__ block_err,
+                                                        uint32_t* __restrict__ err_word, int nblk, int E) {
     __shared__ int tot[512];
+    __shared__ uint32_t err;
     const int e = threadIdx.x;
+    // error word 0: the union of the blocks' error bits
+    if (e == 0) err = 0;
+    __syncthreads();
+    uint32_t bits = 0;
+    for (int b = e; b < nblk; b += 512) bits |= block_err[b];
+    if (bits) atomicOr(&err, bits);
     int run = 0;
     if (e < E) {
         for (int b = 0; b < nblk; ++b) {
@@ -57,6 +85,7 @@ __global__ void __launch_bounds__(512) perm_scan_kernel(const int32_t* __restric
     }
     if (e < E) offsets[e] = tot[e] - run;
     if (e == E - 1) offsets[E] = tot[e];
+    if (e == 0) *err_word = err;   // the scan's barriers ordered every atomicOr before this
 }
 
 // ---------------------------------------------------------------------------
@@ -106,7 +135,8 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
 // exclusive scans (rows and m-tiles), the stable in-block rank of every slot
 // (the ballot match of perm_scatter_kernel) and the per-tile descriptors
 // (max_tiles of them; 0 when the streaming GEMMs run, which need none).
-// One launch instead of four.
+// One launch instead of four.  Writes error word 0, and word 1 (= 0: its own
+// offsets are valid) when it writes a tile plan.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* __restrict__ ids,
                                                                 int32_t* __restrict__ offsets,
@@ -114,7 +144,9 @@ __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* _
                                                                 int32_t* __restrict__ row_of_slot,
                                                                 int32_t* __restrict__ tile_start,
                                                                 int4* __restrict__ tile_info,
+                                                                uint32_t* __restrict__ err_words,
                                                                 int N, int E, int k, int rpt, int max_tiles) {
+    __shared__ uint32_t err;
     __shared__ int cnt[512];
     __shared__ int2 scan[512];          // (rows, tiles) inclusive prefix
     __shared__ int off[513], tst[513];
@@ -122,12 +154,21 @@ __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* _
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < 512; i += kPermBlock) cnt[i] = 0;
     for (int i = tid; i < (kPermBlock / 64) * 512; i += kPermBlock) (&wcnt[0][0])[i] = 0;
+    if (tid == 0) err = 0;
     __syncthreads();
     const int id = tid < N ? ids[tid] : -1;
     const bool valid = (unsigned)id < (unsigned)E;
     const int e = valid ? id : 1023;    // 1023 never equals a real id (E <= 512)
     if (valid) atomicAdd(&cnt[e], 1);   // counts only; no position depends on the order
+    if (tid < N) {
+        const uint32_t bad = slot_error(ids, tid, id, E, k);
+        if (bad) atomicOr(&err, bad);
+    }
     __syncthreads();
+    if (tid == 0) {
+        err_words[0] = err;
+        if (max_tiles > 0) err_words[1] = 0;
+    }
     // inclusive scan of (rows, tiles) over 512 experts: Hillis-Steele on threads 0..511
     int n = 0, nt = 0;
     if (tid < 512) {
@@ -193,24 +234,26 @@ __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* _
 }
 
 hipError_t launch_perm_small(const int32_t* ids, int32_t* offsets, int32_t* sorted_token, int32_t* row_of_slot,
-                             int32_t* tile_start, int4* tile_info, int64_t N, int E, int k, int rows_per_tile,
-                             int max_tiles, hipStream_t stream) {
+                             int32_t* tile_start, int4* tile_info, uint32_t* err_words, int64_t N, int E, int k,
+                             int rows_per_tile, int max_tiles, hipStream_t stream) {
     hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(kPermBlock), 0, stream, ids, offsets, sorted_token,
-                       row_of_slot, tile_start, tile_info, (int)N, E, k, rows_per_tile, max_tiles);
+                       row_of_slot, tile_start, tile_info, err_words, (int)N, E, k, rows_per_tile, max_tiles);
     return hipGetLastError();
 }
 
-hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, int64_t N, int E,
-                             hipStream_t stream) {
+hipError_t launch_perm_count(const int32_t* ids, int32_t* block_counts, uint32_t* block_err, int64_t N, int E,
+                             int k, hipStream_t stream) {
     const int nblk = (int)((N + kPermBlock - 1) / kPermBlock);
-    hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(kPermBlock), 0, stream, ids, block_counts, (int)N, E);
+    hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(kPermBlock), 0, stream, ids, block_counts, block_err,
+                       (int)N, E, k);
     return hipGetLastError();
 }
 
-hipError_t launch_perm_scan(const int32_t* block_counts, int32_t* block_base, int32_t* offsets, int64_t N,
-                            int E, hipStream_t stream) {
+hipError_t launch_perm_scan(const int32_t* block_counts, int32_t* block_base, int32_t* offsets,
+                            const uint32_t* block_err, uint32_t* err_word, int64_t N, int E, hipStream_t stream) {
     const int nblk = (int)((N + kPermBlock - 1) / kPermBlock);
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(512), 0, stream, block_counts, block_base, offsets, nblk, E);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(512), 0, stream, block_counts, block_base, offsets, block_err,
+                       err_word, nblk, E);
     return hipGetLastError();
 }
 
@@ -254,16 +297,25 @@ hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, u
 
 // ---------------------------------------------------------------------------
 // Tile plan of the grouped GEMMs: expert e owns m-tiles
-// [tile_start[e], tile_start[e+1]) of rows_per_tile rows each.
+// [tile_start[e], tile_start[e+1]) of rows_per_tile rows each.  The offsets
+// come from the caller on the staged entry points, so they are checked
+// first: unless 0 = o[0] <= ... <= o[E] = N the plan is empty (the GEMMs do
+// nothing) and error word 1 says why.  Valid offsets give at most
+// ceil(N / rpt) + E = max_tiles tiles.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ tile_start, int4* __restrict__ tile_info,
-                                                        int E, int rpt, int max_tiles) {
+                                                        uint32_t* __restrict__ err_word, int E, int rpt,
+                                                        int max_tiles, int N) {
     __shared__ int tot[512];
     __shared__ int start[513];
     __shared__ int off[513];
     const int e = threadIdx.x;
-    const int o0 = (e < E) ? offsets[e] : 0, o1 = (e < E) ? offsets[e + 1] : 0;
+    int o0 = (e < E) ? offsets[e] : 0, o1 = (e < E) ? offsets[e + 1] : 0;
+    bool bad = o0 > o1 || (e == 0 && o0 != 0) || (e == E - 1 && o1 != N);
+    bad = __syncthreads_or(bad);
+    if (e == 0) *err_word = bad ? kErrExpertOffsets : 0u;
+    if (bad) { o0 = 0; o1 = 0; }   // an empty plan
     const int n = (e < E) ? (o1 - o0 + rpt - 1) / rpt : 0;
     tot[e] = n;
     __syncthreads();
@@ -276,7 +328,7 @@ __global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restric
     if (e < E) { start[e] = tot[e] - n; off[e] = o0; tile_start[e] = tot[e] - n; }
     if (e == E - 1) { start[E] = tot[e]; off[E] = o1; tile_start[E] = tot[e]; }
     __syncthreads();
-    const int ntiles = start[E];
+    const int ntiles = min(start[E], max_tiles);
     for (int t = e; t < max_tiles; t += 512) {
         int4 info = {-1, 0, 0, 0};
         if (t < ntiles) {
@@ -292,10 +344,10 @@ __global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restric
     }
 }
 
-hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, int E, int rows_per_tile,
-                            int max_tiles, hipStream_t stream) {
-    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(512), 0, stream, offsets, tile_start, tile_info, E,
-                       rows_per_tile, max_tiles);
+hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, uint32_t* err_word, int E,
+                            int rows_per_tile, int max_tiles, int64_t N, hipStream_t stream) {
+    hipLaunchKernelGGL(tile_plan_kernel, dim3(1), dim3(512), 0, stream, offsets, tile_start, tile_info, err_word, E,
+                       rows_per_tile, max_tiles, (int)N);
     return hipGetLastError();
 }
 

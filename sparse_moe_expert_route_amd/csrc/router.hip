@@ -370,7 +370,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
         const int e = lane + 64 * j;
         if (e < E) {
             float l = L[e];
-            if constexpr (SIG) l = 1.0f / (1.0f + expf(-l));   // the score replaces the logit
+            // the score replaces the logit: sigmoid evaluated in float64 and
+            // rounded once to float32, so that two implementations of it agree
+            // on the float32 score (and with it on the selection) unless the
+            // float64 value lies within an ulp or two of a float32 midpoint
+            if constexpr (SIG) l = (float)(1.0 / (1.0 + exp(-(double)l)));
             float kf = bias ? l + bias[e] : l;
             lv[j] = l;
             key[j] = ((unsigned long long)ordered_key(kf) << 32) | (uint32_t)(~(uint32_t)e);

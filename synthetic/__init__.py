@@ -179,21 +179,35 @@ def zipf_bias(E, H, seed=0):
     return (-0.55 * sigma * np.log(r)).astype(np.float32)
 
 
+def make_experts(name_or_cfg, seed=0, **over):
+    """The expert weights of a layer: dict(w13, w13_s, w2, w2_s).  They depend only on
+    (H, I, E, format, seed), so layers that differ only in T or bias share them."""
+    cfg = config(name_or_cfg, **over)
+    H, E, inter = cfg["H"], cfg["E"], cfg["I"]
+    out = {}
+    if cfg["format"] == "fp8_block":
+        out["w13"], out["w13_s"] = fp8block_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
+        out["w2"], out["w2_s"] = fp8block_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
+    else:
+        out["w13"], out["w13_s"] = mxfp4_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
+        out["w2"], out["w2_s"] = mxfp4_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
+    return out
+
+
 def make_layer(name_or_cfg, seed=0, experts=True, **over):
     """All inputs of one layer as numpy arrays (see the module docstring for distributions).
 
-    experts=False skips the expert weights (for router-only uses)."""
+    experts=False skips the expert weights (for router-only uses); a dict made by
+    make_experts for the same shapes and seed is used as given."""
     cfg = config(name_or_cfg, **over)
     T, H, E, k, inter = cfg["T"], cfg["H"], cfg["E"], cfg["k"], cfg["I"]
     layer = dict(cfg=cfg, top_k=k, format=cfg["format"])
     layer["x"] = bf16_normal(seed, STREAM_X, (T, H), 1.0)
     layer["w_router"] = bf16_normal(seed, STREAM_WR, (E, H), 0.02)
-    if experts and cfg["format"] == "fp8_block":
-        layer["w13"], layer["w13_s"] = fp8block_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
-        layer["w2"], layer["w2_s"] = fp8block_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
+    if experts is True:
+        layer.update(make_experts(cfg, seed))
     elif experts:
-        layer["w13"], layer["w13_s"] = mxfp4_normal(seed, STREAM_W13, 2 * inter, H, 0.02, batch=E)
-        layer["w2"], layer["w2_s"] = mxfp4_normal(seed, STREAM_W2, H, inter, 0.02, batch=E)
+        layer.update(experts)   # expert arrays made earlier by make_experts for the same shapes and seed
     if cfg["bias"] == "zipf":
         layer["bias"] = zipf_bias(E, H, seed)
     elif cfg["bias"] == "zero":

@@ -9,6 +9,7 @@ Tolerances (written here once, used by every parity test):
     activation FP8 codes and scales, lossless GEMM results): bit-exact.
 """
 
+import collections
 import sys
 
 import numpy as np
@@ -37,6 +38,26 @@ def host(t):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
+
+
+_EXPERT_CACHE = collections.OrderedDict()
+_EXPERT_CACHE_BYTES = 24 << 30
+
+
+def full_layer(name, seed=0):
+    """make_layer(name, seed) with the expert weights shared between workloads of the same
+    (H, I, E, format, seed) within one test session (least recently used dropped past 24 GiB)."""
+    import synthetic as S
+    cfg = S.config(name)
+    key = (cfg["H"], cfg["I"], cfg["E"], cfg["format"], seed)
+    if key in _EXPERT_CACHE:
+        _EXPERT_CACHE.move_to_end(key)
+    else:
+        _EXPERT_CACHE[key] = S.make_experts(name, seed)
+        while len(_EXPERT_CACHE) > 1 and sum(sum(a.nbytes for a in v.values())
+                                             for v in _EXPERT_CACHE.values()) > _EXPERT_CACHE_BYTES:
+            _EXPERT_CACHE.popitem(last=False)
+    return S.make_layer(name, seed=seed, experts=_EXPERT_CACHE[key])
 
 
 def weights(layer, packed=False):

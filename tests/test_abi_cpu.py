@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
     for st, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"), (4, b"HIP launch failure")]:
         assert lib.moe_status_string(st) == text
     assert lib.moe_status_string(99) == b"unknown status"

@@ -23,8 +23,11 @@ import torch
 
 import synthetic as S
 from oracle import checks
+from oracle import formats as F
+from oracle import layer as OL
 from moe_testutil import (dev, host, log, weights, problem, logit_tol, unambiguous_tokens, key_margin, bf16_rne,
-                          oracle_with_allowance, check_output)
+                          oracle_with_allowance, check_output, full_layer, h_rounding_allowance, ACC_REL,
+                          ACC_REL_FP8)
 
 pytestmark = pytest.mark.gpu
 
@@ -159,16 +162,19 @@ def test_staged_entry_points_equal_forward(moe, packed, fmt):
 
 
 # the benchmarked path (packed weights) on every workload, and canonical
-# weights on one decode and one prefill workload
-FULL = [("tiny", True), ("flash_decode", True), ("pro_decode", True), ("flash_prefill", True),
-        ("pro_skewed_prefill", True), ("flash_decode", False), ("flash_prefill", False),
-        # one GPU's share of the 4-way tensor-parallel layer (I = 512)
-        ("flash_decode_tp4", True), ("pro_skewed_prefill_tp4", True),
+# weights on one decode and one prefill workload; grouped by expert weight set
+# (Flash, Pro, their tensor-parallel shares, FP8 block-scaled) so that the
+# weights are generated once per set
+FULL = [("tiny", True), ("flash_decode", True), ("flash_decode", False), ("flash_prefill", True),
+        ("flash_prefill", False),
         # speculative-decoding verify blocks (32 sequences x 8 positions)
-        ("flash_verify", True), ("pro_verify", True),
+        ("flash_verify", True),
+        ("pro_decode", True), ("pro_skewed_prefill", True), ("pro_verify", True),
+        # one GPU's share of the 4-way tensor-parallel layer (I = 512), all four workloads
+        ("flash_decode_tp4", True), ("flash_prefill_tp4", True), ("pro_decode_tp4", True),
+        ("pro_skewed_prefill_tp4", True),
         # FP8 block-scaled experts
-        ("flash_decode_fp8", True), ("flash_decode_fp8", False), ("pro_decode_fp8", True),
-        ("flash_prefill_fp8", True)]
+        ("flash_decode_fp8", True), ("flash_decode_fp8", False), ("flash_prefill_fp8", True), ("pro_decode_fp8", True)]
 # sigmoid scoring at full size: zero bias (Flash decode) and the Zipf
 # selection bias (Pro skewed prefill)
 FULL_SIGMOID = [("flash_decode", True), ("pro_skewed_prefill", True)]
@@ -179,7 +185,7 @@ FULL_SIGMOID = [("flash_decode", True), ("pro_skewed_prefill", True)]
                          [pytest.param(c, pk, "sigmoid", id="sigmoid-%s" % c) for c, pk in FULL_SIGMOID])
 def test_forward_full_size_sampled(moe, cfg, packed, score):
     log("full-size %s packed=%s score=%s: generating layer" % (cfg, packed, score))
-    lay = S.make_layer(cfg, seed=0)
+    lay = full_layer(cfg)
     lay["score"] = score
     p = problem(lay)
     T, H = lay["x"].shape
@@ -213,6 +219,146 @@ def test_forward_full_size_sampled(moe, cfg, packed, score):
     err, share = check_output(y[toks], ref, rows=clear)
     log("  max err / RMS = %.3e (%d of %d sampled tokens unambiguous); beyond the plain bar: %.2e"
         % (err, clear.sum(), len(toks), share))
+
+
+# ---------------------------------------------------------------------------
+# Full size, staged, whole experts.  The stages run on the GPU one after the
+# other on the workload's seeded inputs, each fed the previous stage's GPU
+# output (the staging of the oracle comparison: routing from the GPU's
+# logits, GEMM-2 on the GPU's h), and every row of a chosen set of experts is
+# compared with the oracle:
+#   * permutation of every slot: bit-exact (oracle counting sort of the GPU's ids);
+#   * FP8 activation codes and scales of the chosen rows: bit-exact;
+#   * h codes and scales: equal except where the oracle flags the rounding as
+#     ambiguous (reading R16; FP8 block-scaled experts: every scale inside the
+#     interval the accumulation error allows);
+#   * y_perm: within ACC_REL * sum|h w| of the oracle's down projection of the
+#     GPU's own h (no allowance for anything else);
+#   * the combine on 256 sampled tokens: within k float32 roundings of the
+#     weighted sum of the GPU's own y_perm rows;
+#   * the fused forward equals the staged path bit for bit on every token.
+# The chosen experts: the most and the least loaded, the owners of the first
+# and last work item of each XCD's share of the LDS-tiled GEMMs' item lists
+# (both GEMMs), and a few more at random.  The most loaded expert of the
+# skewed workload has ~10k rows: 80 m-tiles of 128 rows in chunks of four,
+# the last one partial.
+# ---------------------------------------------------------------------------
+STAGED_FULL = ["flash_decode", "flash_prefill", "pro_decode", "pro_skewed_prefill", "flash_prefill_tp4",
+               "pro_skewed_prefill_tp4", "flash_prefill_fp8"]
+
+
+def _xcd_boundary_experts(counts, NB, rows_per_tile=128, xcds=8):
+    tiles = (counts + rows_per_tile - 1) // rows_per_tile
+    ts = np.concatenate([[0], np.cumsum(tiles)])
+    total = int(ts[-1]) * NB
+    out = set()
+    for x in range(xcds):
+        lo, hi = (total * x) // xcds, (total * (x + 1)) // xcds
+        for item in ((lo, hi - 1) if lo < hi else ()):
+            out.add(int(np.searchsorted(ts, item // NB, side="right") - 1))
+    return out
+
+
+def _check_h(gq, gs, fl, fmt):
+    """GPU h codes/scales of one expert's rows against the oracle's, under the flag rule."""
+    gv, rv = F.decode_e4m3(gq), F.decode_e4m3(fl["hq"])
+    if fmt == "fp8_block":
+        g64 = gs.astype(np.float64)
+        assert np.all((g64 >= fl["scale_lo"]) & (g64 <= fl["scale_hi"])), "h scale outside its interval"
+        differ = gv != rv
+        bmax = np.abs(gv).reshape(gv.shape[0], -1, 128).max(-1)
+        assert np.all(bmax[g64 > 0] == 448.0)
+    else:
+        assert np.all(fl["block"][gs != fl["hs"]]), "an h scale differs where the oracle flags nothing"
+        differ = (gv != rv) & np.repeat(gs == fl["hs"], 128, axis=1)
+    assert np.all(fl["element"][differ]), "an h code differs where the oracle flags nothing"
+    return int(differ.sum()), int(fl["element"].sum())
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", STAGED_FULL)
+def test_staged_full_size_whole_experts(moe, cfg):
+    log("staged full-size %s: generating layer" % cfg)
+    lay = full_layer(cfg)
+    p = problem(lay)
+    fmt = OL.expert_format(lay)
+    T, H = lay["x"].shape
+    E, k, inter = p.num_experts, p.top_k, p.intermediate
+    N = T * k
+    W = weights(lay, True)
+    ws = moe.alloc_workspace(p)
+    x = dev(lay["x"])
+    b = None if lay["bias"] is None else dev(lay["bias"])
+    sdt = moe.scale_dtype(p)
+    L = torch.empty(T, E, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    st = torch.empty(N, dtype=torch.int32, device="cuda")
+    ros = torch.empty(N, dtype=torch.int32, device="cuda")
+    xq = torch.empty(N, H, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(N, H // 128, dtype=sdt, device="cuda")
+    hq = torch.empty(N, inter, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(N, inter // 128, dtype=sdt, device="cuda")
+    yp = torch.empty(N, H, device="cuda")
+    y = torch.empty(T, H, device="cuda")
+    log("  stages on the GPU")
+    moe.route(p, x, dev(lay["w_router"]), b, L, ids, w)
+    moe.permute(p, ids, x, off, st, ros, xq, xs, ws)
+    moe.grouped_gemm1_swiglu(p, xq, xs, off, W, hq, hs, ws)
+    moe.grouped_gemm2(p, hq, hs, off, W, yp, ws)
+    moe.combine(p, yp, ros, w, y)
+    assert moe.error_words(ws) == (0, 0)
+    y_fused = torch.empty(T, H, device="cuda")
+    moe.forward(p, x, dev(lay["w_router"]), b, W, y_fused, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fused, y), "the fused forward differs from the staged path"
+    assert moe.error_words(ws) == (0, 0)
+    ids_g, w_g = host(ids), host(w)
+    checks.check_routing(ids_g, w_g, E)
+    ref = OL.permutation(ids_g, E)
+    off_g, st_g, ros_g = host(off), host(st), host(ros)
+    assert np.array_equal(off_g, ref["offsets"])
+    assert np.array_equal(st_g, ref["sorted_token"])
+    assert np.array_equal(ros_g, ref["row_of_slot"])
+    counts = np.diff(off_g).astype(np.int64)
+    touched = np.nonzero(counts)[0]
+    rng = np.random.default_rng(7)
+    sel = {int(np.argmax(counts)), int(touched[np.argmin(counts[touched])]), int(touched[0]), int(touched[-1])}
+    if N >= 32 * E:   # the LDS-tiled kernels' persistent item split
+        sel |= _xcd_boundary_experts(counts, inter // 256) | _xcd_boundary_experts(counts, H // 512)
+    sel |= {int(e) for e in rng.choice(touched, size=min(4, len(touched)), replace=False)}
+    sel = sorted(sel)
+    log("  experts %s with %s rows (%d of %d rows)" % (sel, counts[sel].tolist(), counts[sel].sum(), N))
+    acc = ACC_REL_FP8 if fmt == "fp8_block" else ACC_REL
+    worst, n_diff, n_flag = 0.0, 0, 0
+    for e in sel:
+        r0, r1 = int(off_g[e]), int(off_g[e + 1])
+        tok = st_g[r0:r1]
+        qx, sx = OL.quantize_activations(lay["x"][tok], fmt)
+        assert np.array_equal(host(xq[r0:r1]), qx) and np.array_equal(host(xs[r0:r1]), sx), "x codes, expert %d" % e
+        a = F.dequantize_fp8_blocks_f32(qx, sx) if fmt == "fp8_block" else F.dequantize_fp8_blocks(qx, sx)
+        _, _, fl = h_rounding_allowance(a, lay["w13"][e], lay["w13_s"][e], lay["w2"][e], lay["w2_s"][e], fmt=fmt)
+        gq, gs = host(hq[r0:r1]), host(hs[r0:r1])
+        d, f = _check_h(gq, gs, fl, fmt)
+        n_diff, n_flag = n_diff + d, n_flag + f
+        Hd = F.dequantize_fp8_blocks_f32(gq, gs) if fmt == "fp8_block" else F.dequantize_fp8_blocks(gq, gs)
+        W2 = OL.decode_expert_matrix(lay["w2"][e], lay["w2_s"][e], fmt)
+        y_ref = Hd @ W2.T
+        bound = acc * (np.abs(Hd) @ np.abs(W2).T) + 1e-30
+        dy = np.abs(host(yp[r0:r1]).astype(np.float64) - y_ref)
+        assert np.all(dy <= bound), "y_perm of expert %d: %.3e of the bound" % (e, float(np.max(dy / bound)))
+        worst = max(worst, float(np.max(dy / bound)))
+    log("  h codes differing from the oracle: %d (all flagged; %d flagged); y_perm within %.2f of the "
+        "accumulation bound" % (n_diff, n_flag, worst))
+    # combine on sampled tokens, from the GPU's own y_perm rows
+    toks = np.sort(rng.choice(T, size=min(T, 256), replace=False))
+    rows = ros_g.reshape(T, k)[toks]
+    Yp = host(yp[torch.from_numpy(rows.reshape(-1).astype(np.int64)).cuda()]).reshape(len(toks), k, H).astype(np.float64)
+    wt = w_g[toks].astype(np.float64)[:, :, None]
+    ref_y = np.sum(wt * Yp, axis=1)
+    bound = k * np.finfo(np.float32).eps * np.sum(np.abs(wt * Yp), axis=1) + 1e-30
+    assert np.all(np.abs(host(y)[toks] - ref_y) <= bound)
 
 
 # ---------------------------------------------------------------------------
