@@ -8,7 +8,7 @@ resident in HBM.
 Prints ONE JSON line:
   value        tokens/s of the whole layer: T tokens / the median step time, each
                step timed alone with HIP events around moe_forward after a 1 GiB
-               write that evicts the L2s and the 256 MB last-level cache (the
+               read that evicts the L2s and the 256 MB last-level cache (the
                timed loop is exactly `steps` such steps, bracketed by device
                synchronisations); `warm` is the rate of `steps` back-to-back
                steps with no flush
@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-flush", action="store_true",
                     help="time the steps without the 1 GiB cache flush before each (value = warm rate)")
+    ap.add_argument("--flush", choices=["read", "write"], default="read",
+                    help="how the cache flush touches its 1 GiB: read it (default; leaves no dirty lines whose "
+                         "write-back the next step would pay for) or write it")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens for the CPU oracle (0 = auto)")
     ap.add_argument("--canonical-weights", action="store_true",
                     help="run on the canonical (row-major) weight layout instead of the packed one")
@@ -163,17 +166,21 @@ def main():
     log("bench: warm %.3f ms/step, %.0f tokens/s" % (warm["ms_per_step"], warm["value"]))
 
     # ---- the timed loop: exactly `steps` steps with cold caches.  Before each step a
-    # 1 GiB write evicts the L2s and the 256 MB last-level cache, then HIP events on the
+    # 1 GiB read evicts the L2s and the 256 MB last-level cache (a write would leave dirty
+    # lines there whose write-back lands in the next step), then HIP events on the
     # launching stream bracket moe_forward alone; value = T / median step time ----
     flushed = None
-    scratch = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    scratch = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     times = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         if scratch is not None:
-            scratch.fill_(1.0)
+            if args.flush == "read":
+                torch.sum(scratch, dtype=torch.float32)
+            else:
+                scratch.fill_(1.0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         moe.forward(p, x, wr, bias, W, y, ws)
@@ -187,7 +194,8 @@ def main():
     ms_per_step = float(q[1])
     tokens_per_s = T / (ms_per_step * 1e-3)
     flushed = {"ms_p10": round(float(q[0]), 4), "ms_median": round(float(q[1]), 4), "ms_p90": round(float(q[2]), 4),
-               "flush": not args.no_flush, "loop_wall_ms_per_step": round(loop_wall / args.steps * 1e3, 4)}
+               "flush": None if args.no_flush else "%s 1 GiB" % args.flush,
+               "loop_wall_ms_per_step": round(loop_wall / args.steps * 1e3, 4)}
     log("bench: %s step median %.3f ms (p10 %.3f, p90 %.3f), %.0f tokens/s"
         % ("cold-cache" if not args.no_flush else "event-timed", q[1], q[0], q[2], tokens_per_s))
 

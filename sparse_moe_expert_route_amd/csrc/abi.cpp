@@ -6,7 +6,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include "moe.h"
-#include "moe_internal.h"
+#include "moe_launch.h"
 
 namespace {
 

@@ -51,7 +51,7 @@ constexpr int kF8ItemRows = 32 * kF8Waves;     // weight rows per item
 constexpr int kF8MChunk = 4;                   // m-tiles of one expert scheduled together
 constexpr int kF8TT = kF8TileRows / 32;        // token tiles per m-tile
 constexpr int kF8ActLoads = kF8TileRows * kF8StageK / 16 / (64 * kF8Waves);   // 16-byte loads per lane per stage
-constexpr int kF8MaxKB = 64;                   // 128-deep K blocks the LDS weight-scale copy holds (K <= 8192)
+constexpr int kF8MaxKB = kF8TiledMaxK / 128;    // 128-deep K blocks the LDS weight-scale copy holds
 
 // One LDS block, scales first: every operand read of the K loop then sits
 // below 64 KB, in reach of the 16-bit immediate offset of a DS instruction
@@ -81,10 +81,12 @@ struct F8Item {
 };
 
 __device__ __forceinline__ F8Item f8_item_at(const GemmArgs& a, int item, int NB) {
-    // items of expert e: [NB * tile_start[e], NB * tile_start[e+1]); its m-tiles
-    // in chunks of kF8MChunk, n-block major, m-tile minor within a chunk
-    const int e = a.tile_info[item / NB].x;
-    const int t0 = a.tile_start[e], nt = a.tile_start[e + 1] - t0;
+    // items of expert e: [NB * t0, NB * (t0 + nt)) with t0 its first tile in
+    // the plan and nt = ceil(n_e / 128) its tiles; its m-tiles in chunks of
+    // kF8MChunk, n-block major, m-tile minor within a chunk
+    const int4 head = a.tile_info[item / NB];
+    const int e = head.x, t0 = head.w;
+    const int nt = (a.offsets[e + 1] - a.offsets[e] + kF8TileRows - 1) / kF8TileRows;
     const int local = item - NB * t0;
     const int full = nt / kF8MChunk;
     const int chunk = min(local / (kF8MChunk * NB), full);
@@ -345,9 +347,6 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
     }
 }
 
-bool fp8_tiled_gemm_supported(int H, int I) {
-    return H % 512 == 0 && I % 512 == 0 && H <= 128 * kF8MaxKB && I <= 128 * kF8MaxKB;
-}
 
 static int f8_persistent_grid() {
     static int cached = 0;

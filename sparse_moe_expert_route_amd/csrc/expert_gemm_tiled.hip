@@ -18,11 +18,11 @@
 //
 // Work decomposition: an item is (m-tile of 128 rows of one expert, block of
 // 512 weight rows): 256 features (gate and up rows) of the gate/up GEMM, or
-// 512 output features of the down GEMM.  A workgroup has 4 waves, one per
-// SIMD; each wave owns 4 weight tiles of 32 rows (in registers, loaded
+// 512 output features of the down GEMM.  A workgroup has 8 waves, two per
+// SIMD; each wave owns 2 weight tiles of 32 rows (in registers, loaded
 // straight from memory) and multiplies them with the 4 token tiles of the
-// m-tile (from LDS), so every activation operand read from LDS feeds four
-// MFMAs.  The 256 accumulators of a wave live in the accumulation registers.
+// m-tile (from LDS), so every activation operand read from LDS feeds two
+// MFMAs.  The 128 accumulators of a wave are 2 x 4 32x32 tiles.
 //
 // Pipeline: the activation tile of a stage (128 rows x 256 bytes) is staged
 // by direct global->LDS loads (no staging registers) into a ring of four
@@ -59,7 +59,7 @@ constexpr int kWaves = 8;                 // waves per workgroup, two per SIMD
 constexpr int kWT = 2;                    // 32-row weight tiles per wave
 constexpr int kTT = kTileRows / 32;       // 32-row token tiles per m-tile
 constexpr int kItemRows = 32 * kWT * kWaves;   // weight rows per item (512)
-constexpr int kMaxK = 6144;               // largest K the LDS scale copies hold
+constexpr int kMaxK = kTiledMaxK;         // largest K the LDS scale copies hold
 constexpr int kActDma = kTileRows * kStageK / 1024 / kWaves;   // 1 KB activation loads per wave per stage
 constexpr int kWaveRows = kTileRows / kWaves;   // activation rows each wave stages
 constexpr int kBlkWaves = kFp8Block / (16 * kWT);   // waves holding one 128-feature block (gate/up)
@@ -97,6 +97,11 @@ constexpr int kXscLoads = (kMaxK / kFp8Block / 2 + kWaves - 1) / kWaves;
 __shared__ __attribute__((aligned(16))) uint8_t tl_xsc[2 * kXscBytes];
 // per-row maxima of the SwiGLU epilogue
 __shared__ float tl_red[kWaves * kTileRows];
+// down-GEMM epilogue: one 16-row x 32-feature fp32 tile per wave (rows padded
+// to 36 floats so the 16-byte writes of a row's two lane halves and the
+// row-order reads spread over the banks)
+constexpr int kOutPitch = 36;
+__shared__ __attribute__((aligned(16))) float tl_out[kWaves * 16 * kOutPitch];
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9
 // encoding, vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
@@ -139,9 +144,9 @@ constexpr int kWaitStep0 = 3 * kWT + kActDma;
 constexpr int kWaitStepN = 2 * kWT + kActDma + kWT + kWT;
 static_assert(kWaitStepN == 3 * kWT + kActDma + kWT, "step wait");
 
-// A work item (wave-uniform).
+// A work item (wave-uniform); ntt = 32-row token tiles that hold rows.
 struct Item {
-    int e, row0, nrows, nblk;
+    int e, row0, nrows, nblk, ntt;
 };
 
 // Activation rows of one item that this lane loads (with the gather fused,
@@ -152,11 +157,14 @@ struct Rows {
 };
 
 __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
-    // items of expert e: [NB * tile_start[e], NB * tile_start[e+1]).  Its
-    // m-tiles go in chunks of kMChunk; within a chunk the order is n-block
-    // major, m-tile minor.
-    const int e = a.tile_info[item / NB].x;
-    const int t0 = a.tile_start[e], nt = a.tile_start[e + 1] - t0;
+    // items of expert e: [NB * t0, NB * (t0 + nt)) with t0 its first tile in
+    // the plan and nt = ceil(n_e / 128) its tiles.  Its m-tiles go in chunks of
+    // kMChunk; within a chunk the order is n-block major, m-tile minor.  The
+    // item multiplies the expert's token-tile class: its tiles' height / 32.
+    const int4 head = a.tile_info[item / NB];
+    const int e = head.x, t0 = head.w;
+    const int ne = a.offsets[e + 1] - a.offsets[e];
+    const int nt = (ne + kTileRows - 1) / kTileRows;
     const int local = item - NB * t0;
     const int full = nt / kMChunk;
     const int chunk = min(local / (kMChunk * NB), full);
@@ -166,7 +174,8 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
     const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
     // every lane computes the same item: keep it in scalar registers
     return Item{__builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(ti.y),
-                __builtin_amdgcn_readfirstlane(ti.z), __builtin_amdgcn_readfirstlane(nblk)};
+                __builtin_amdgcn_readfirstlane(ti.z), __builtin_amdgcn_readfirstlane(nblk),
+                __builtin_amdgcn_readfirstlane(tile_height(ne, nt) >> 5)};
 }
 
 // The persistent loop of one workgroup.  LDS buffers come in as restrict
@@ -176,7 +185,8 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
 template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
 __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
                                            uint8_t* __restrict__ act2, uint8_t* __restrict__ act3,
-                                           uint8_t* __restrict__ xsc, float* __restrict__ red) {
+                                           uint8_t* __restrict__ xsc, float* __restrict__ red,
+                                           float* __restrict__ out_tile) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, r = lane & 31;
@@ -318,10 +328,11 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
     // landed; starts the row lookups of the next item); KIND 2: its second
     // (starts the copy of the next item's activation scales).  SET: which
     // weight-scale set the stage reads.
-    auto stage = [&](auto bufc, auto setc, auto kindc, int st) {
+    auto stage = [&](auto bufc, auto setc, auto kindc, auto nttc, int st) {
         constexpr int BUF = decltype(bufc)::value;
         constexpr int SET = decltype(setc)::value;
         constexpr int KIND = decltype(kindc)::value;
+        constexpr int NTT = decltype(nttc)::value;   // token tiles multiplied (the rest hold no rows)
         constexpr int NBUF = (BUF + DA) % 4;
         // this stage's activations, scales and first weights have landed in
         // every wave, and every wave is done with the buffer the prefetch
@@ -332,10 +343,10 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         const uint8_t* xs = xsc + xpar * kXscBytes;
         // activation scale byte of each token tile (128-channel block 2st + g)
         const int xb = 2 * st + g;
-        int bs[kTT];
+        int bs[NTT];
 #pragma unroll
-        for (int j = 0; j < kTT; ++j) bs[j] = xs[4 * ((xb >> 2) * kTileRows + 32 * j + r) + (xb & 3)];
-        v8i B[kTT];
+        for (int j = 0; j < NTT; ++j) bs[j] = xs[4 * ((xb >> 2) * kTileRows + 32 * j + r) + (xb & 3)];
+        v8i B[NTT];
         auto read_b = [&](int j, int s) {
             const int row = 32 * j + r;
             const uint4 lo4 = *(const uint4*)(lds + swz(row, 2 * s + g));
@@ -344,7 +355,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
             B[j][4] = hi4.x; B[j][5] = hi4.y; B[j][6] = hi4.z; B[j][7] = hi4.w;
         };
 #pragma unroll
-        for (int j = 0; j < kTT; ++j) read_b(j, 0);
+        for (int j = 0; j < NTT; ++j) read_b(j, 0);
         if constexpr (KIND == 1) lookup_rows(inxt, nxt);
         if constexpr (KIND == 2) dma_xsc(nxt.xrow, xsc + (xpar ^ 1) * kXscBytes);
         // prefetch targets: weights of the next stage, activations DA stages
@@ -378,8 +389,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                 asm volatile("s_nop 0");
                 __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int j = 0; j < kTT; ++j) {
+            auto mfmas = [&](int j) {
 #pragma unroll
                 for (int t = 0; t < kWT; ++t) {
                     const uint4 w = wreg[s][t];
@@ -393,66 +403,93 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                     }
                 }
                 if (s < 3) read_b(j, s + 1);
-                if (s == 0 && j == 0) {
+            };
+            mfmas(0);
+            if (s == 0) {
 #pragma unroll
-                    for (int t = 0; t < kWT; ++t) wsc[SET ^ 1][t] = bload4(rs, sl[t], wst * SST);
-                }
-                if (j == kTT - 1) {
-                    // step s is done with its weights: refill them with the next stage's
+                for (int t = 0; t < kWT; ++t) wsc[SET ^ 1][t] = bload4(rs, sl[t], wst * SST);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int t = 0; t < kWT; ++t) wreg[s][t] = bload16(rw, wl[t], wst * WST + s * WSS);
-                    if (s == 3) dma_act(std::integral_constant<int, NBUF>{}, arow, ast, 0, kActDma);
-                }
+            for (int j = 1; j < NTT; ++j) {
+                mfmas(j);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // step s is done with its weights: refill them with the next stage's
+#pragma unroll
+            for (int t = 0; t < kWT; ++t) wreg[s][t] = bload16(rw, wl[t], wst * WST + s * WSS);
+            if (s == 3) dma_act(std::integral_constant<int, NBUF>{}, arow, ast, 0, kActDma);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     // The stages of one item; B0 = ring buffer of its first stage (0, or 2
-    // when the stage count is 2 mod 4 and the item is odd).
-    auto run_item = [&](auto b0c) {
+    // when the stage count is 2 mod 4 and the item is odd); NTT = its token
+    // tiles.
+    auto run_item = [&](auto b0c, auto nttc) {
         constexpr int B0 = decltype(b0c)::value;
         using S0 = std::integral_constant<int, 0>;
         using S1 = std::integral_constant<int, 1>;
         using KN = std::integral_constant<int, 0>;
-        stage(std::integral_constant<int, B0>{}, S0{}, std::integral_constant<int, 1>{}, 0);
-        stage(std::integral_constant<int, (B0 + 1) % 4>{}, S1{}, std::integral_constant<int, 2>{}, 1);
+        stage(std::integral_constant<int, B0>{}, S0{}, std::integral_constant<int, 1>{}, nttc, 0);
+        stage(std::integral_constant<int, (B0 + 1) % 4>{}, S1{}, std::integral_constant<int, 2>{}, nttc, 1);
         int st = 2;
         for (; st + 4 <= nstage; st += 4) {
-            stage(std::integral_constant<int, (B0 + 2) % 4>{}, S0{}, KN{}, st);
-            stage(std::integral_constant<int, (B0 + 3) % 4>{}, S1{}, KN{}, st + 1);
-            stage(std::integral_constant<int, B0>{}, S0{}, KN{}, st + 2);
-            stage(std::integral_constant<int, (B0 + 1) % 4>{}, S1{}, KN{}, st + 3);
+            stage(std::integral_constant<int, (B0 + 2) % 4>{}, S0{}, KN{}, nttc, st);
+            stage(std::integral_constant<int, (B0 + 3) % 4>{}, S1{}, KN{}, nttc, st + 1);
+            stage(std::integral_constant<int, B0>{}, S0{}, KN{}, nttc, st + 2);
+            stage(std::integral_constant<int, (B0 + 1) % 4>{}, S1{}, KN{}, nttc, st + 3);
         }
         if (st < nstage) {
-            stage(std::integral_constant<int, (B0 + 2) % 4>{}, S0{}, KN{}, st);
-            stage(std::integral_constant<int, (B0 + 3) % 4>{}, S1{}, KN{}, st + 1);
+            stage(std::integral_constant<int, (B0 + 2) % 4>{}, S0{}, KN{}, nttc, st);
+            stage(std::integral_constant<int, (B0 + 3) % 4>{}, S1{}, KN{}, nttc, st + 1);
         }
     };
 
-    // Epilogue of the current item, then move on to the next; false past the
-    // workgroup's last item.
-    auto finish_item = [&]() -> bool {
+    // Epilogue of the current item (NTT token tiles), then move on to the
+    // next; false past the workgroup's last item.
+    auto finish_item = [&](auto nttc) -> bool {
+        constexpr int NTT = decltype(nttc)::value;
         // ---- epilogue: lane holds tokens 32j + r and tile rows 8*(i/4) + 4g + (i%4) ----
         const int row0 = icur.row0, nrows = icur.nrows, nblk = icur.nblk;
         if constexpr (MODE == kGemm2) {
+            // fp32 rows through a wave-private LDS tile, so that each store
+            // instruction writes 8 whole 128-byte lines (8 lanes per row)
+            // instead of 32-byte pieces of 32 lines: per (token tile j,
+            // weight tile t) and half h of the 32 rows, the lanes holding rows
+            // 16h .. 16h+15 put their 16 features of the row into the tile,
+            // then every lane reads one 16-byte chunk of a row back.  LDS
+            // operations of one wave run in order, so no barrier is needed.
+            float* ot = out_tile + wave * (16 * kOutPitch);
 #pragma unroll
-            for (int j = 0; j < kTT; ++j) {
-                // uniform base plus a 32-bit lane offset
-                if (r >= nrows - 32 * j) continue;
-                float* ob = (float*)a.out + ((size_t)(row0 + 32 * j) * a.H + nblk * kItemRows + 32 * kWT * wave);
-                const uint32_t lo = (uint32_t)(r * a.H + 4 * g);
+            for (int j = 0; j < NTT; ++j) {
+                if (32 * j >= nrows) break;   // token tiles past the item's rows hold nothing
 #pragma unroll
-                for (int t = 0; t < kWT; ++t)
+                for (int t = 0; t < kWT; ++t) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *(v4f*)(ob + (lo + 32 * t + 8 * q)) =
-                            v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2], acc[t][j][4 * q + 3]};
+                    for (int h = 0; h < 2; ++h) {
+                        if ((r >> 4) == h) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                *(v4f*)(ot + (r & 15) * kOutPitch + 8 * q + 4 * g) =
+                                    v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2], acc[t][j][4 * q + 3]};
+                        }
+                        // uniform base plus a 32-bit lane offset
+                        float* ob = (float*)a.out + ((size_t)(row0 + 32 * j + 16 * h) * a.H + nblk * kItemRows +
+                                                     32 * kWT * wave + 32 * t);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int row = 8 * u + (lane >> 3), ch = lane & 7;
+                            const v4f v = *(const v4f*)(ot + row * kOutPitch + 4 * ch);
+                            if (32 * j + 16 * h + row < nrows) *(v4f*)(ob + (uint32_t)(row * a.H + 4 * ch)) = v;
+                        }
+                    }
+                }
             }
         } else if constexpr (MODE == kGemm1Preact) {
             // tile row 8q + 4g + i: q = 0, 1 gate features f + 8q + 4g + i, q = 2, 3 up
 #pragma unroll
-            for (int j = 0; j < kTT; ++j) {
+            for (int j = 0; j < NTT; ++j) {
                 if (r >= nrows - 32 * j) continue;
                 float* o = (float*)a.out + (size_t)(row0 + 32 * j) * (2 * a.I) + (uint32_t)(r * 2 * a.I);
 #pragma unroll
@@ -470,9 +507,9 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
             // SwiGLU on matching gate (element i) and up (element i + 8)
             // values, then FP8 over 128 features: waves 2b and 2b + 1 hold
             // the features of block b of the item
-            float amax[kTT];
+            float amax[NTT];
 #pragma unroll
-            for (int j = 0; j < kTT; ++j) {
+            for (int j = 0; j < NTT; ++j) {
                 float m = 0.0f;
 #pragma unroll
                 for (int t = 0; t < kWT; ++t)
@@ -488,11 +525,11 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
             }
             if (g == 0) {
 #pragma unroll
-                for (int j = 0; j < kTT; ++j) red[wave * kTileRows + 32 * j + r] = amax[j];
+                for (int j = 0; j < NTT; ++j) red[wave * kTileRows + 32 * j + r] = amax[j];
             }
             __syncthreads();
 #pragma unroll
-            for (int j = 0; j < kTT; ++j) {
+            for (int j = 0; j < NTT; ++j) {
                 const int rr = 32 * j + r;
                 const int w0 = wave - wave % kBlkWaves;
                 float m = red[w0 * kTileRows + rr];
@@ -543,24 +580,43 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
 
     // With a stage count of 2 mod 4 consecutive items start at ring buffers 0
     // and 2, so items go in pairs; the ring position of every stage stays a
-    // compile-time constant either way.
+    // compile-time constant either way.  Those kernels run every item on all
+    // four token tiles.  The others run each item on its expert's token-tile
+    // class, a compile-time constant in one loop per class: the plan lists the
+    // classes in the order 4, 3, 2, 1, so a workgroup goes through the loops
+    // once, in that order, and the items that share a weight block (the
+    // m-tiles of one expert, all of one class) run the same stage bodies.
+    using T4 = std::integral_constant<int, 4>;
     if constexpr (PAIR) {
         for (;;) {
-            run_item(I0{});
-            if (!finish_item()) break;
-            run_item(I2{});
-            if (!finish_item()) break;
+            run_item(I0{}, T4{});
+            if (!finish_item(T4{})) break;
+            run_item(I2{}, T4{});
+            if (!finish_item(T4{})) break;
         }
     } else {
-        do {
-            run_item(I0{});
-        } while (finish_item());
+        bool more = true;
+        auto run_class = [&](auto nttc) {
+            while (more && icur.ntt == decltype(nttc)::value) {
+                run_item(I0{}, nttc);
+                more = finish_item(nttc);
+            }
+        };
+        run_class(T4{});
+        run_class(std::integral_constant<int, 3>{});
+        run_class(std::integral_constant<int, 2>{});
+        run_class(std::integral_constant<int, 1>{});
     }
 }
 
 template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
 __global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmArgs a) {
-    tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red);
+    // only the down GEMM's epilogue uses the output tile (its LDS is not
+    // allocated for the gate/up kernels)
+    if constexpr (MODE == kGemm2)
+        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, tl_out);
+    else
+        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, nullptr);
 }
 
 static int persistent_grid() {
@@ -574,9 +630,6 @@ static int persistent_grid() {
     return cached;
 }
 
-bool tiled_gemm_supported(int H, int I) {
-    return H % 512 == 0 && I % 512 == 0 && H <= kMaxK && I <= kMaxK;
-}
 
 template <int MODE, bool PACKED, bool GATHER>
 static void launch_tiled_variant(const GemmArgs& a, hipStream_t stream) {

@@ -130,6 +130,86 @@ __global__ void __launch_bounds__(1024) perm_scatter_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Tile plan of the LDS-tiled grouped GEMMs, by one workgroup of at least 512
+// threads from the expert offsets off[0..E] in LDS.  Expert e with n_e rows
+// gets nt_e = ceil(n_e / rpt) m-tiles of height h_e = tile_height(n_e, nt_e)
+// (its last tile holds the rest) and the token-tile class c_e = h_e / 32:
+// the number of 32-row token tiles its items multiply.  Tiles are listed class
+// by class (4, 3, 2, 1), experts in id order within a class and the tiles of
+// one expert consecutive, so that the GEMM's workgroups move through the
+// classes in one direction.  Writes tile_start[e] = first tile of expert e
+// (tile_start[E] = number of tiles) and tile_info[t] = {expert, first row,
+// rows, first tile of the expert} for t < max_tiles (expert -1 past the
+// last tile).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int comp(const int4& v, int s) { return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w; }
+
+__device__ void class_tile_plan(const int* __restrict__ off, int E, int rpt, int max_tiles,
+                                int32_t* __restrict__ tile_start, int4* __restrict__ tile_info) {
+    __shared__ int4 sc_t[512];       // inclusive prefix over experts of their tiles, per class slot 4 - c
+    __shared__ int4 sc_n[512];       // ... of the experts that have tiles
+    __shared__ int sstart[513], sexp[512];   // first tile and expert of the r-th expert in list order
+    const int tid = threadIdx.x;
+    int n = 0, nt = 0, c = 0;
+    if (tid < E) {
+        n = off[tid + 1] - off[tid];
+        nt = (n + rpt - 1) / rpt;
+        c = nt ? tile_height(n, nt) / 32 : 0;
+    }
+    const int slot = 4 - c;   // class 4 first
+    if (tid < 512) {
+        sc_t[tid] = int4{slot == 0 ? nt : 0, slot == 1 ? nt : 0, slot == 2 ? nt : 0, slot == 3 ? nt : 0};
+        sc_n[tid] = int4{c && slot == 0, c && slot == 1, c && slot == 2, c && slot == 3};
+    }
+    __syncthreads();
+    for (int d = 1; d < 512; d <<= 1) {
+        int4 vt = int4{0, 0, 0, 0}, vn = int4{0, 0, 0, 0};
+        if (tid < 512 && tid >= d) { vt = sc_t[tid - d]; vn = sc_n[tid - d]; }
+        __syncthreads();
+        if (tid < 512) {
+            sc_t[tid].x += vt.x; sc_t[tid].y += vt.y; sc_t[tid].z += vt.z; sc_t[tid].w += vt.w;
+            sc_n[tid].x += vn.x; sc_n[tid].y += vn.y; sc_n[tid].z += vn.z; sc_n[tid].w += vn.w;
+        }
+        __syncthreads();
+    }
+    const int4 Tt = sc_t[511], Tn = sc_n[511];
+    const int total = Tt.x + Tt.y + Tt.z + Tt.w, listed = Tn.x + Tn.y + Tn.z + Tn.w;
+    if (tid < E) {
+        int first = 0;
+        if (c) {
+            int bt = 0, bn = 0;
+            for (int q = 0; q < slot; ++q) { bt += comp(Tt, q); bn += comp(Tn, q); }
+            first = bt + comp(sc_t[tid], slot) - nt;
+            const int rank = bn + comp(sc_n[tid], slot) - 1;
+            sstart[rank] = first;
+            sexp[rank] = tid;
+        }
+        tile_start[tid] = first;
+    }
+    if (tid == 0) {
+        tile_start[E] = total;
+        sstart[listed] = total;
+    }
+    __syncthreads();
+    for (int t = tid; t < max_tiles; t += blockDim.x) {
+        int4 info = {-1, 0, 0, 0};
+        if (t < total) {
+            int lo = 0, hi = listed - 1;   // the last listed expert whose first tile is <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sstart[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            const int e = sexp[lo], t0 = sstart[lo];
+            const int ne = off[e + 1] - off[e];
+            const int h = tile_height(ne, (ne + rpt - 1) / rpt);
+            const int row0 = off[e] + (t - t0) * h;
+            info = int4{e, row0, min(h, off[e + 1] - row0), t0};
+        }
+        tile_info[t] = info;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // All of the permutation for at most kPermBlock slots (decode), plus the
 // tiled GEMMs' tile plan, in one workgroup: expert histogram, the two
 // exclusive scans (rows and m-tiles), the stable in-block rank of every slot
@@ -148,8 +228,8 @@ __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* _
                                                                 int N, int E, int k, int rpt, int max_tiles) {
     __shared__ uint32_t err;
     __shared__ int cnt[512];
-    __shared__ int2 scan[512];          // (rows, tiles) inclusive prefix
-    __shared__ int off[513], tst[513];
+    __shared__ int scan[512];           // inclusive prefix of the rows
+    __shared__ int off[513];
     __shared__ int wcnt[kPermBlock / 64][512];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int i = tid; i < 512; i += kPermBlock) cnt[i] = 0;
@@ -169,30 +249,27 @@ __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* _
         err_words[0] = err;
         if (max_tiles > 0) err_words[1] = 0;
     }
-    // inclusive scan of (rows, tiles) over 512 experts: Hillis-Steele on threads 0..511
-    int n = 0, nt = 0;
+    // inclusive scan of the rows over 512 experts: Hillis-Steele on threads 0..511
+    int n = 0;
     if (tid < 512) {
         n = tid < E ? cnt[tid] : 0;
-        nt = (n + rpt - 1) / rpt;
-        scan[tid] = int2{n, nt};
+        scan[tid] = n;
     }
     __syncthreads();
     for (int d = 1; d < 512; d <<= 1) {
-        int2 v = int2{0, 0};
+        int v = 0;
         if (tid < 512 && tid >= d) v = scan[tid - d];
         __syncthreads();
-        if (tid < 512) { scan[tid].x += v.x; scan[tid].y += v.y; }
+        if (tid < 512) scan[tid] += v;
         __syncthreads();
     }
     if (tid < E) {
-        off[tid] = scan[tid].x - n;
-        tst[tid] = scan[tid].y - nt;
-        offsets[tid] = scan[tid].x - n;
-        tile_start[tid] = scan[tid].y - nt;
+        off[tid] = scan[tid] - n;
+        offsets[tid] = scan[tid] - n;
     }
     if (tid == E - 1) {
-        off[E] = scan[tid].x; tst[E] = scan[tid].y;
-        offsets[E] = scan[tid].x; tile_start[E] = scan[tid].y;
+        off[E] = scan[tid];
+        offsets[E] = scan[tid];
     }
     // stable rank of each slot among the slots of its expert
     unsigned long long m = ~0ull;
@@ -216,20 +293,10 @@ __global__ void __launch_bounds__(kPermBlock) perm_small_kernel(const int32_t* _
             row_of_slot[tid] = -1;   // an out-of-range id gets no row
         }
     }
-    // per-tile descriptors {expert, first row, rows}; expert -1 past the last tile
-    const int ntiles = tst[E];
-    for (int t = tid; t < max_tiles; t += kPermBlock) {
-        int4 info = {-1, 0, 0, 0};
-        if (t < ntiles) {
-            int lo = 0, hi = E - 1;   // largest expert whose first tile is <= t
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (tst[mid] <= t) lo = mid; else hi = mid - 1;
-            }
-            const int row0 = off[lo] + (t - tst[lo]) * rpt;
-            info = int4{lo, row0, min(rpt, off[lo + 1] - row0), 0};
-        }
-        tile_info[t] = info;
+    // the tiled GEMMs' tile plan (max_tiles is 0 when the streaming GEMMs run)
+    if (max_tiles > 0) {
+        __syncthreads();   // off[] complete
+        class_tile_plan(off, E, rpt, max_tiles, tile_start, tile_info);
     }
 }
 
@@ -296,52 +363,27 @@ hipError_t launch_quant_gather(const uint16_t* x, const int32_t* sorted_token, u
 }
 
 // ---------------------------------------------------------------------------
-// Tile plan of the grouped GEMMs: expert e owns m-tiles
-// [tile_start[e], tile_start[e+1]) of rows_per_tile rows each.  The offsets
-// come from the caller on the staged entry points, so they are checked
-// first: unless 0 = o[0] <= ... <= o[E] = N the plan is empty (the GEMMs do
-// nothing) and error word 1 says why.  Valid offsets give at most
+// Tile plan of the grouped GEMMs from caller-given offsets (class_tile_plan).
+// The offsets come from the caller on the staged entry points, so they are
+// checked first: unless 0 = o[0] <= ... <= o[E] = N the plan is empty (the
+// GEMMs do nothing) and error word 1 says why.  Valid offsets give at most
 // ceil(N / rpt) + E = max_tiles tiles.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(512) tile_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ tile_start, int4* __restrict__ tile_info,
                                                         uint32_t* __restrict__ err_word, int E, int rpt,
                                                         int max_tiles, int N) {
-    __shared__ int tot[512];
-    __shared__ int start[513];
     __shared__ int off[513];
     const int e = threadIdx.x;
-    int o0 = (e < E) ? offsets[e] : 0, o1 = (e < E) ? offsets[e + 1] : 0;
+    const int o0 = (e < E) ? offsets[e] : 0, o1 = (e < E) ? offsets[e + 1] : 0;
     bool bad = o0 > o1 || (e == 0 && o0 != 0) || (e == E - 1 && o1 != N);
     bad = __syncthreads_or(bad);
     if (e == 0) *err_word = bad ? kErrExpertOffsets : 0u;
-    if (bad) { o0 = 0; o1 = 0; }   // an empty plan
-    const int n = (e < E) ? (o1 - o0 + rpt - 1) / rpt : 0;
-    tot[e] = n;
+    // invalid offsets: every expert empty, an empty plan
+    if (e < E) off[e] = bad ? 0 : o0;
+    if (e == E - 1) off[E] = bad ? 0 : o1;
     __syncthreads();
-    for (int d = 1; d < 512; d <<= 1) {
-        const int v = (e >= d) ? tot[e - d] : 0;
-        __syncthreads();
-        tot[e] += v;
-        __syncthreads();
-    }
-    if (e < E) { start[e] = tot[e] - n; off[e] = o0; tile_start[e] = tot[e] - n; }
-    if (e == E - 1) { start[E] = tot[e]; off[E] = o1; tile_start[E] = tot[e]; }
-    __syncthreads();
-    const int ntiles = min(start[E], max_tiles);
-    for (int t = e; t < max_tiles; t += 512) {
-        int4 info = {-1, 0, 0, 0};
-        if (t < ntiles) {
-            int lo = 0, hi = E - 1;   // largest expert whose first tile is <= t
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (start[mid] <= t) lo = mid; else hi = mid - 1;
-            }
-            const int row0 = off[lo] + (t - start[lo]) * rpt;
-            info = int4{lo, row0, min(rpt, off[lo + 1] - row0), 0};
-        }
-        tile_info[t] = info;
-    }
+    class_tile_plan(off, E, rpt, max_tiles, tile_start, tile_info);
 }
 
 hipError_t launch_tile_plan(const int32_t* offsets, int32_t* tile_start, int4* tile_info, uint32_t* err_word, int E,

@@ -26,8 +26,8 @@ from oracle import checks
 from oracle import formats as F
 from oracle import layer as OL
 from moe_testutil import (dev, host, log, weights, problem, logit_tol, unambiguous_tokens, key_margin, bf16_rne,
-                          oracle_with_allowance, check_output, full_layer, h_rounding_allowance, ACC_REL,
-                          ACC_REL_FP8)
+                          oracle_with_allowance, check_output, full_layer, h_rounding_allowance, ACC_REL_FP8,
+                          ACC_REL_GEMM2)
 
 pytestmark = pytest.mark.gpu
 
@@ -232,8 +232,9 @@ def test_forward_full_size_sampled(moe, cfg, packed, score):
 #   * h codes and scales: equal except where the oracle flags the rounding as
 #     ambiguous (reading R16; FP8 block-scaled experts: every scale inside the
 #     interval the accumulation error allows);
-#   * y_perm: within ACC_REL * sum|h w| of the oracle's down projection of the
-#     GPU's own h (no allowance for anything else);
+#   * y_perm: within ACC_REL_GEMM2 * sum|h w| (the measured float32 accumulation
+#     bound of the down projection) of the oracle's down projection of the GPU's
+#     own h (no allowance for anything else);
 #   * the combine on 256 sampled tokens: within k float32 roundings of the
 #     weighted sum of the GPU's own y_perm rows;
 #   * the fused forward equals the staged path bit for bit on every token.
@@ -330,7 +331,7 @@ def test_staged_full_size_whole_experts(moe, cfg):
     sel |= {int(e) for e in rng.choice(touched, size=min(4, len(touched)), replace=False)}
     sel = sorted(sel)
     log("  experts %s with %s rows (%d of %d rows)" % (sel, counts[sel].tolist(), counts[sel].sum(), N))
-    acc = ACC_REL_FP8 if fmt == "fp8_block" else ACC_REL
+    acc = max(ACC_REL_FP8, ACC_REL_GEMM2) if fmt == "fp8_block" else ACC_REL_GEMM2
     worst, n_diff, n_flag = 0.0, 0, 0
     for e in sel:
         r0, r1 = int(off_g[e]), int(off_g[e + 1])
@@ -345,12 +346,14 @@ def test_staged_full_size_whole_experts(moe, cfg):
         Hd = F.dequantize_fp8_blocks_f32(gq, gs) if fmt == "fp8_block" else F.dequantize_fp8_blocks(gq, gs)
         W2 = OL.decode_expert_matrix(lay["w2"][e], lay["w2_s"][e], fmt)
         y_ref = Hd @ W2.T
-        bound = acc * (np.abs(Hd) @ np.abs(W2).T) + 1e-30
+        ssum = np.abs(Hd) @ np.abs(W2).T + 1e-300
         dy = np.abs(host(yp[r0:r1]).astype(np.float64) - y_ref)
-        assert np.all(dy <= bound), "y_perm of expert %d: %.3e of the bound" % (e, float(np.max(dy / bound)))
-        worst = max(worst, float(np.max(dy / bound)))
-    log("  h codes differing from the oracle: %d (all flagged; %d flagged); y_perm within %.2f of the "
-        "accumulation bound" % (n_diff, n_flag, worst))
+        worst = max(worst, float(np.max(dy / ssum)))
+        log("    expert %d: %d rows, %d h codes differ (all flagged), max |dy| / sum|h w| = %.2e"
+            % (e, r1 - r0, d, float(np.max(dy / ssum))))
+    log("  h codes differing from the oracle: %d (all flagged; %d flagged); max |dy| / sum|h w| = %.3e (bound %.1e)"
+        % (n_diff, n_flag, worst, acc))
+    assert worst <= acc
     # combine on sampled tokens, from the GPU's own y_perm rows
     toks = np.sort(rng.choice(T, size=min(T, 256), replace=False))
     rows = ros_g.reshape(T, k)[toks]

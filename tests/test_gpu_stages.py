@@ -17,6 +17,7 @@ from oracle import checks
 from oracle import formats as F
 from oracle import layer as OL
 from moe_testutil import (dev, host, log, weights, logit_tol, unambiguous_tokens, key_margin, WEIGHT_ATOL, ACC_REL,
+                          ACC_REL_GEMM2,
                           h_rounding_allowance, pack_codes_reference, pack_scales_reference)
 
 pytestmark = pytest.mark.gpu
@@ -398,3 +399,50 @@ def test_gemm1_accumulation_error_bound(moe, T, H, I, E, k):
             worst = max(worst, float(d.max()))
     log("  max |g_gpu - g| / sum|a w| = %.3e (bound %.1e)" % (worst, ACC_REL))
     assert worst <= ACC_REL
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(64, 4096, 2048, 8, 8), (64, 4096, 512, 8, 8), (300, 1024, 512, 8, 4),
+                                       (300, 6144, 512, 8, 4), (400, 4096, 2048, 8, 8), (40, 1024, 640, 12, 3)])
+def test_gemm2_accumulation_error_bound(moe, T, H, I, E, k):
+    """The down projection of real SwiGLU h codes (the oracle's, from a random layer) is
+    within ACC_REL_GEMM2 * sum|h_k w_k| of the exact float64 product: the premise of the
+    y_perm bar of the full-size staged tests.  Also logs the error against the largest
+    single product, eps32 * max_k |h_k w_k|, to show which of the two it follows."""
+    lay = S.make_layer("tiny", seed=13, T=T, H=H, I=I, E=E, k=k)
+    log("gemm2 accumulation bound T=%d H=%d I=%d E=%d" % (T, H, I, E))
+    N = T * k
+    ids = S.random_ids(T, E, k, seed=14)
+    perm = OL.permutation(ids, E)
+    xq, xs = OL.quantize_activations(lay["x"])
+    A = F.dequantize_fp8_blocks(xq, xs)[perm["sorted_token"]]
+    off = perm["offsets"]
+    hq = np.zeros((N, I), np.uint8)
+    hs = np.zeros((N, I // 128), np.uint8)
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            o = OL.expert_ffn(A[r0:r1], lay["w13"][e], lay["w13_s"][e], lay["w2"][e], lay["w2_s"][e])
+            hq[r0:r1], hs[r0:r1] = o["hq"], o["hs"]
+    p = moe.Problem.make(T, H, I, E, k)
+    ws = moe.alloc_workspace(p)
+    y = torch.empty(N, H, dtype=torch.float32, device="cuda")
+    moe.grouped_gemm2(p, dev(hq), dev(hs), dev(off), weights(lay, True), y, ws)
+    torch.cuda.synchronize()
+    Hd = F.dequantize_fp8_blocks(hq, hs)
+    g = host(y).astype(np.float64)
+    worst, at = 0.0, None
+    eps = float(np.finfo(np.float32).eps)
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 > r0:
+            W2 = F.decode_mxfp4(lay["w2"][e], lay["w2_s"][e])
+            d = np.abs(g[r0:r1] - Hd[r0:r1] @ W2.T) / (np.abs(Hd[r0:r1]) @ np.abs(W2).T + 1e-300)
+            i = np.unravel_index(np.argmax(d), d.shape)
+            if d[i] > worst:
+                prods = np.abs(Hd[r0 + i[0]] * W2[i[1]])
+                at = (e, float(d[i]), float(np.abs(g[r0 + i[0], i[1]] - Hd[r0 + i[0]] @ W2[i[1]]) / (eps * prods.max())),
+                      int(np.count_nonzero(prods)))
+                worst = float(d[i])
+    log("  max |y_gpu - y| / sum|h w| = %.3e (bound %.1e); at that element: expert %d, error = %.2f eps32 * max|h_k w_k|, "
+        "%d non-zero products" % (worst, ACC_REL_GEMM2, at[0], at[2], at[3]))
+    assert worst <= ACC_REL_GEMM2
