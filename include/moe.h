@@ -273,6 +273,30 @@ moe_status moe_forward(const moe_problem* problem, const void* x_bf16, const voi
                        const float* sel_bias, const moe_expert_weights* weights, void* y,
                        int32_t out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Size of the scratch array behind moe_forward_noalloc (96 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, computation, kernels and results as moe_forward, without the
+ * workspace: the library keeps it in a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES on every device it runs on (held until the process
+ * ends), found on the first call on each device.  Nothing is allocated and no
+ * allocating routine is called.  The caller still provides the inputs and y.
+ * Limits: moe_workspace_size(problem) <= MOE_NOALLOC_SCRATCH_BYTES, which
+ * covers the decode and speculative-verify batches (up to 2048 routed rows
+ * at hidden 6144); a larger problem returns MOE_ERR_WORKSPACE_TOO_SMALL
+ * before anything is enqueued.  Every call on one device shares that device's
+ * array and leaves its own intermediates there (no part of it needs to start
+ * at zero: each call writes everything it reads), so calls that can overlap
+ * on one device (other streams, other host threads) race: order them, or use
+ * moe_forward with a workspace each.  The device error words of the call are
+ * at moe_error_words_offset() in the array; they cannot be read without its
+ * address, so this entry point is for callers that do not check them.      */
+moe_status moe_forward_noalloc(const moe_problem* problem, const void* x_bf16, const void* w_router_bf16,
+                               const float* sel_bias, const moe_expert_weights* weights, void* y,
+                               int32_t out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "MoeError", "Problem", "ExpertWeights", "lib_path", "load", "abi_version", "workspace_size",
     "alloc_workspace", "prepack_weights", "route", "permute", "grouped_gemm_swiglu", "grouped_gemm1_swiglu",
-    "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "OUT_F32", "OUT_BF16",
+    "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "forward_noalloc", "OUT_F32", "OUT_BF16",
     "WEIGHTS_CANONICAL", "WEIGHTS_PACKED", "EXPERTS_MXFP4", "EXPERTS_FP8_BLOCK", "EXPORTED_SYMBOLS",
     "scale_dtype", "error_words", "DEVERR_EXPERT_ID_RANGE", "DEVERR_EXPERT_ID_DUPLICATE", "DEVERR_EXPERT_OFFSETS",
 ]
@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = [
     "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_error_words_offset", "moe_prepack_weights",
     "moe_route", "moe_permute",
     "moe_grouped_gemm_swiglu", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_preact",
-    "moe_grouped_gemm2", "moe_combine", "moe_forward",
+    "moe_grouped_gemm2", "moe_combine", "moe_forward", "moe_forward_noalloc",
 ]
 
 
@@ -138,6 +138,7 @@ def load():
     L.moe_grouped_gemm2.argtypes = [P, vp, vp, vp, W, vp, vp, sz, vp]
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, i32, vp]
     L.moe_forward.argtypes = [P, vp, vp, vp, W, vp, i32, vp, sz, vp]
+    L.moe_forward_noalloc.argtypes = [P, vp, vp, vp, W, vp, i32, vp]
     for name in EXPORTED_SYMBOLS:
         if name not in ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_error_words_offset"):
             getattr(L, name).restype = ctypes.c_int
@@ -322,3 +323,23 @@ def forward(p, x, w_router, sel_bias, weights, y, ws, out_dtype=OUT_F32, stream=
     st = load().moe_forward(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(sel_bias), ctypes.byref(w), _ptr(y),
                             int(out_dtype), _ptr(ws), ws.numel(), _stream(stream))
     _raise("moe_forward", st)
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20   # MOE_NOALLOC_SCRATCH_BYTES of moe.h
+
+
+def forward_noalloc(p, x, w_router, sel_bias, weights, y, out_dtype=OUT_F32, stream=None):
+    """moe_forward without a workspace: the library's static scratch array on the current
+    device holds the intermediates (problems up to NOALLOC_SCRATCH_BYTES of workspace).
+    Calls that overlap on one device share that array."""
+    T, H, E = p.num_tokens, p.hidden, p.num_experts
+    _check(x, torch.bfloat16, (T, H), "x")
+    _check(w_router, torch.bfloat16, (E, H), "w_router")
+    if sel_bias is not None:
+        _check(sel_bias, torch.float32, (E,), "sel_bias")
+    weights.check(p)
+    _check(y, torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, (T, H), "y")
+    w = weights.struct()
+    st = load().moe_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(sel_bias), ctypes.byref(w),
+                                    _ptr(y), int(out_dtype), _stream(stream))
+    _raise("moe_forward_noalloc", st)

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["abi.cpp", "router.hip", "permute.hip", "prepack.hip", "expert_gemm.hip", "expert_gemm_tiled.hip",
-           "expert_gemm_fp8.hip", "expert_gemm_fp8_tiled.hip", "combine.hip"]
+           "expert_gemm_fp8.hip", "expert_gemm_fp8_tiled.hip", "combine.hip", "noalloc.hip"]
 HEADERS = ["moe_launch.h", "moe_internal.h", "fp8_rows.h"]
 ARCH = "gfx950"
 

@@ -133,6 +133,17 @@ moe_status run_route(const moe_problem& p, const void* x, const void* wr, const 
 
 bool use_tiled(const moe_problem& p);
 
+moe_status check_forward_args(const moe_problem* p, const void* x_bf16, const void* w_router_bf16,
+                              const float* sel_bias, const moe_expert_weights* weights, const void* y,
+                              int32_t out_dtype) {
+    MOE_CHECK(check_problem(p));
+    MOE_CHECK(check_weights(weights));
+    if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    if (!all_aligned(x_bf16, w_router_bf16, y)) return MOE_ERR_INVALID_ARGUMENT;
+    if (sel_bias && !aligned16(sel_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    return MOE_OK;
+}
+
 // Permutation and FP8 gather.  Up to kPermBlock slots (decode) one workgroup
 // does the whole permutation and, when the tiled GEMMs will run, also writes
 // their tile plan into the workspace (the streaming GEMMs need none);
@@ -396,11 +407,7 @@ moe_status moe_combine(const moe_problem* p, const float* y_perm, const int32_t*
 moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_router_bf16, const float* sel_bias,
                        const moe_expert_weights* weights, void* y, int32_t out_dtype, void* ws, size_t ws_bytes,
                        hipStream_t stream) {
-    MOE_CHECK(check_problem(p));
-    MOE_CHECK(check_weights(weights));
-    if (out_dtype != MOE_OUT_F32 && out_dtype != MOE_OUT_BF16) return MOE_ERR_INVALID_ARGUMENT;
-    if (!all_aligned(x_bf16, w_router_bf16, y)) return MOE_ERR_INVALID_ARGUMENT;
-    if (sel_bias && !aligned16(sel_bias)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_CHECK(check_forward_args(p, x_bf16, w_router_bf16, sel_bias, weights, y, out_dtype));
     MOE_CHECK(check_ws(*p, ws, ws_bytes));
     if (p->num_tokens == 0) return MOE_OK;
     const Layout L = layout_of(*p);
@@ -430,3 +437,17 @@ moe_status moe_forward(const moe_problem* p, const void* x_bf16, const void* w_r
 }
 
 }  // extern "C"
+
+extern "C" moe_status moe_forward_noalloc(const moe_problem* p, const void* x_bf16, const void* w_router_bf16,
+                                          const float* sel_bias, const moe_expert_weights* weights, void* y,
+                                          int32_t out_dtype, hipStream_t stream) {
+    MOE_CHECK(check_forward_args(p, x_bf16, w_router_bf16, sel_bias, weights, y, out_dtype));
+    if (p->num_tokens == 0) return MOE_OK;
+    if (layout_of(*p).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    // the scratch array's device address on the current device (found once per
+    // device), used exactly as moe_forward uses a caller's workspace
+    void* ws = noalloc_scratch();
+    if (!ws) return MOE_ERR_HIP;
+    return moe_forward(p, x_bf16, w_router_bf16, sel_bias, weights, y, out_dtype, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                       stream);
+}

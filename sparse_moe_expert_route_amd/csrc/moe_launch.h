@@ -126,6 +126,11 @@ inline bool fp8_tiled_gemm_supported(int H, int I) {
 }
 hipError_t launch_expert_gemm_fp8_tiled(GemmMode mode, const GemmArgs& a, hipStream_t stream);
 
+// Device address of the current device's copy of the moe_forward_noalloc
+// scratch array (MOE_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once
+// per device; null if the HIP runtime reports an error.
+void* noalloc_scratch();
+
 hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y,
                           int out_bf16, int64_t T, int H, int k, hipStream_t stream);
 

@@ -125,3 +125,18 @@ def test_prepack_launches(lib, fmt, expect):
     outs = [ctypes.c_void_p(A + (q << 34)) for q in (4, 5, 6, 7)]
     st, d = _delta(lib, lambda: lib.moe_prepack_weights(ctypes.byref(p), ctypes.byref(w), *outs, None))
     assert st == 0 and d == expect
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(64, 4096, 2048, 256, 8), (256, 6144, 2048, 384, 8)])
+def test_forward_noalloc_runs_the_forward_in_the_scratch_array(lib, T, H, I, E, k):
+    """The same launches as moe_forward, with the scratch array as the workspace."""
+    p = moe.Problem.make(T, H, I, E, k)
+    ws = lib.moe_workspace_size(ctypes.byref(p))
+    w = _w(1)
+    vp = ctypes.c_void_p
+    st, d_ref = _delta(lib, lambda: lib.moe_forward(ctypes.byref(p), vp(A), vp(A), None, ctypes.byref(w), vp(A), 0,
+                                                    vp(A), ws, None))
+    assert st == 0
+    st, d = _delta(lib, lambda: lib.moe_forward_noalloc(ctypes.byref(p), vp(A), vp(A), None, ctypes.byref(w), vp(A),
+                                                        0, None))
+    assert st == 0 and d == d_ref

@@ -129,6 +129,28 @@ def test_invalid_arguments_rejected_before_launch(lib):
     assert lib.moe_route(ctypes.byref(ps), None, None, None, vp(FAKE), vp(FAKE), vp(FAKE), None) == 2
 
 
+def test_forward_noalloc_validates_before_touching_the_gpu(lib):
+    """Invalid arguments and problems whose workspace exceeds the scratch array are refused,
+    and zero tokens return at once, all before any HIP call (there is no GPU here)."""
+    vp = ctypes.c_void_p
+    w = _w()
+    p = _P()
+    assert lib.moe_forward_noalloc(None, vp(FAKE), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 0, None) == 1
+    assert lib.moe_forward_noalloc(ctypes.byref(p), vp(FAKE + 4), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 0,
+                                   None) == 1
+    assert lib.moe_forward_noalloc(ctypes.byref(p), vp(FAKE), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 5,
+                                   None) == 1
+    assert lib.moe_forward_noalloc(ctypes.byref(_P(T=0)), vp(FAKE), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 0,
+                                   None) == 0
+    # Flash prefill needs far more than the 96 MiB array; Pro verify (64.6 MiB) fits
+    big = _P(T=8192, H=4096, I=2048, E=256, k=8)
+    assert lib.moe_workspace_size(ctypes.byref(big)) > moe.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(ctypes.byref(big), vp(FAKE), vp(FAKE), None, ctypes.byref(w), vp(FAKE), 0,
+                                   None) == 3
+    fits = _P(T=256, H=6144, I=2048, E=384, k=8)
+    assert lib.moe_workspace_size(ctypes.byref(fits)) <= moe.NOALLOC_SCRATCH_BYTES
+
+
 def test_zero_tokens_is_a_no_op(lib):
     vp = ctypes.c_void_p
     p = _P(T=0)
