@@ -65,15 +65,23 @@ def parse():
                     help="run on the canonical (row-major) weight layout instead of the packed one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB copy kernel (for scaling HBM byte counters)")
+    ap.add_argument("--micro", action="store_true",
+                    help="run the microbenchmarks of the HBM and MFMA ceilings (include/moe_micro.h) instead, "
+                         "and print their JSON line")
     return ap.parse_args()
 
 
+# the sources the gate/up GEMM's HBM traffic depends on (kernels, shared headers, the tile plan)
 GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm.hip",
                 "sparse_moe_expert_route_amd/csrc/expert_gemm_tiled.hip",
-                "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
+                "sparse_moe_expert_route_amd/csrc/moe_internal.h",
+                "sparse_moe_expert_route_amd/csrc/moe_launch.h",
+                "sparse_moe_expert_route_amd/csrc/permute.hip"]
 FP8_GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm_fp8.hip",
                     "sparse_moe_expert_route_amd/csrc/expert_gemm_fp8_tiled.hip",
-                    "sparse_moe_expert_route_amd/csrc/moe_internal.h"]
+                    "sparse_moe_expert_route_amd/csrc/moe_internal.h",
+                    "sparse_moe_expert_route_amd/csrc/moe_launch.h",
+                    "sparse_moe_expert_route_amd/csrc/permute.hip"]
 
 
 def measured_traffic(workload, sources):
@@ -104,6 +112,9 @@ def main():
         print("bench.py measures one GPU: the library has no multi-GPU path (one layer's expert set fits one "
               "MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.micro:
+        print(json.dumps(micro()), flush=True)
+        return
     import numpy as np
     import torch
 
@@ -309,6 +320,83 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(lay, args, T)
     print(json.dumps(out), flush=True)
+
+
+def micro():
+    """The ceilings the layer is measured against, on this GPU: HBM stream bandwidth (16-byte
+    reads over 4 GiB, two access patterns, a sweep of grid sizes; 16-byte writes) and the
+    block-scaled MFMA issue rate with the shader clock it ran at (libmoe_micro.so)."""
+    import ctypes
+    import numpy as np
+    import torch
+    from sparse_moe_expert_route_amd import build as B
+    if not os.path.exists(B.MICRO_LIB):
+        raise RuntimeError("libmoe_micro.so is not built: run python -m sparse_moe_expert_route_amd.build")
+    L = ctypes.CDLL(B.MICRO_LIB)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.moe_micro_hbm_read.argtypes = [vp, sz, vp, i32, i32, vp]
+    L.moe_micro_hbm_write.argtypes = [vp, sz, i32, vp]
+    L.moe_micro_mfma.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp]
+    stream = torch.cuda.current_stream()
+    sp = vp(stream.cuda_stream)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    out = {"device": torch.cuda.get_device_name(0), "cus": torch.cuda.get_device_properties(0).multi_processor_count}
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(16384 * 256, dtype=torch.int32, device="cuda")
+    hbm = {}
+    for pattern, name in ((0, "read_grid_stride"), (1, "read_chunk_per_workgroup")):
+        res = {}
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            def run(g=grid, pt=pattern):
+                assert L.moe_micro_hbm_read(vp(buf.data_ptr()), nbytes, vp(sink.data_ptr()), g, pt, sp) == 0
+            res[grid] = round(nbytes / timed(run) / 1e9, 1)
+        hbm[name] = {"GB/s by grid": res, "best GB/s": max(res.values())}
+        log("micro: %s %s" % (name, res))
+    res = {}
+    for grid in (2048, 8192):
+        def runw(g=grid):
+            assert L.moe_micro_hbm_write(vp(buf.data_ptr()), nbytes, g, sp) == 0
+        res[grid] = round(nbytes / timed(runw) / 1e9, 1)
+    hbm["write_grid_stride"] = {"GB/s by grid": res, "best GB/s": max(res.values())}
+    log("micro: write %s" % res)
+    hbm["bytes"] = nbytes
+    out["hbm"] = hbm
+    del buf
+    cus = out["cus"]
+    mf = {}
+    fo = torch.empty(cus * 2 * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    for shape, per in ((32, 8 * 2 * 32 * 32 * 64), (16, 16 * 2 * 16 * 16 * 128)):
+        for fa, fb, fname in ((4, 0, "fp4 x fp8"), (0, 0, "fp8 x fp8"), (4, 4, "fp4 x fp4")):
+            for wg_per_cu in (1, 2):
+                grid, iters = cus * wg_per_cu, 4096
+                def runm(g=grid, it=iters, a=fa, b=fb, sh=shape):
+                    assert L.moe_micro_mfma(a, b, sh, it, g, vp(fo.data_ptr()), vp(clk.data_ptr()), sp) == 0
+                t = timed(runm, reps=3)
+                c = clk.cpu().tolist()
+                ghz = c[0] / (c[1] / 100e6) / 1e9 if c[1] else None
+                flops = grid * 4 * iters * per
+                key = "%dx%dx%d %s, %d wave%s per SIMD" % (shape, shape, 64 if shape == 32 else 128, fname, wg_per_cu,
+                                                          "s" if wg_per_cu > 1 else "")
+                mf[key] = {"TFLOP/s": round(flops / t / 1e12, 1), "shader_clock_GHz": round(ghz, 3) if ghz else None}
+                log("micro: %s %s" % (key, mf[key]))
+    out["mfma"] = mf
+    return {"micro": out}
 
 
 def _cpu_model():

@@ -19,6 +19,9 @@ LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["abi.cpp", "router.hip", "permute.hip", "prepack.hip", "expert_gemm.hip", "expert_gemm_tiled.hip",
            "expert_gemm_fp8.hip", "expert_gemm_fp8_tiled.hip", "combine.hip", "noalloc.hip"]
 HEADERS = ["moe_launch.h", "moe_internal.h", "fp8_rows.h"]
+# the microbenchmarks of the HBM and MFMA ceilings (include/moe_micro.h), a library of their own
+MICRO_SOURCES = ["micro.hip"]
+MICRO_LIB = os.path.join(HERE, "libmoe_micro.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -45,12 +48,24 @@ def _run(cmd):
     return res.returncode, _filter(res.stdout)
 
 
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
+    rc, out = _run([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp])
+    if rc != 0:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+        raise RuntimeError("hipcc link failed:\n" + out)
+    os.replace(tmp, lib)
+
+
 def build(verbose=False, jobs=None):
-    """Compile every HIP/C++ source and link the shared library; always rebuilds."""
+    """Compile every HIP/C++ source and link the layer's library and the microbenchmark
+    library; always rebuilds."""
     os.makedirs(OBJ, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    srcs = SOURCES + MICRO_SOURCES
     objs, cmds = [], []
-    for s in SOURCES:
+    for s in srcs:
         o = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
         objs.append(o)
         lang = ["-x", "hip"] if s.endswith(".hip") else []
@@ -58,20 +73,15 @@ def build(verbose=False, jobs=None):
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 4)), 8)
     with ThreadPoolExecutor(jobs) as ex:
         results = list(ex.map(_run, cmds))
-    errors = [(s, out) for s, (rc, out) in zip(SOURCES, results) if rc != 0]
+    errors = [(s, out) for s, (rc, out) in zip(srcs, results) if rc != 0]
     if errors:
         raise RuntimeError("hipcc failed:\n" + "\n".join("== %s ==\n%s" % e for e in errors))
     if verbose:
-        for s, (_, out) in zip(SOURCES, results):
+        for s, (_, out) in zip(srcs, results):
             if out.strip():
                 print("== %s ==\n%s" % (s, out))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    rc, out = _run([hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp])
-    if rc != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
-        raise RuntimeError("hipcc link failed:\n" + out)
-    os.replace(tmp, LIB)
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], MICRO_LIB)
     return LIB
 
 

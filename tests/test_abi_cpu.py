@@ -36,6 +36,19 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_micro_library_exports_every_declared_symbol():
+    """The microbenchmark library (include/moe_micro.h) loads without a GPU and exports its calls."""
+    from sparse_moe_expert_route_amd import build as B
+    if not os.path.exists(B.MICRO_LIB):
+        B.build()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_micro.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_micro_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["moe_micro_hbm_read", "moe_micro_hbm_write", "moe_micro_mfma"]
+    L = ctypes.CDLL(B.MICRO_LIB)
+    for n in names:
+        assert hasattr(L, n), n
+
+
 def test_version_and_status_strings(lib):
     assert moe.abi_version() == 5
     for st, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"), (4, b"HIP launch failure")]:
