@@ -13,7 +13,8 @@ table row "Routed experts"; the vLLM recipe, "Overview"):
     largest finite 448).
   * BF16 router weights and activations: the top 16 bits of an IEEE binary32.
   * FP8 block-scaled expert weights (the earlier V2.5 expert format, same
-    table): e4m3 codes, one float32 scale per 128 x 128 block.
+    table): e4m3 codes; every 128-row by 128-column tile of a matrix carries a
+    float32 multiplier of its own.
 
 Every decoder maps codes to float64 exactly; none rounds.
 """
@@ -195,10 +196,11 @@ def dequantize_fp8_blocks(codes, scales, block=FP8_BLOCK):
 
 
 # ---------------------------------------------------------------------------
-# FP8 block-scaled experts (teardown "Why Are the V2.6 Files Half the Size of
-# V2.5?", table row "Routed experts", V2.5 column: FP8 E4M3 with one F32 scale
-# per 128 x 128 block; vLLM recipe "Overview": computed as block-wise e4m3 at
-# 128 x 128 granularity).
+# FP8 block-scaled experts: the earlier (V2.5) storage of the routed experts in
+# the teardown's table "Why Are the V2.6 Files Half the Size of V2.5?" (e4m3
+# codes, each square tile of 128 rows by 128 columns sharing a single float32
+# multiplier); the vLLM recipe's "Overview" has the arithmetic done in e4m3
+# with that block granularity.
 # ---------------------------------------------------------------------------
 
 def decode_fp8_block(codes, scales, block=FP8_BLOCK):

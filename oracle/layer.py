@@ -6,16 +6,15 @@ What the layer is (the pages, by section):
   * teardown "What Did Xiaomi Release?": 256 routed experts per layer (Flash)
     or 384 (Pro), 8 active per token;
   * teardown "How Big Is Each Expert?": a router picks 8 experts per token;
-    each expert is a gate, an up and a down projection around a 2,048-wide
-    middle layer;
+    three matrices per expert (gate, up, down) with intermediate width I = 2048;
   * teardown "How Is the Backbone Built?" and devupai "No shared expert":
     there is no shared expert, so the output is the routed sum alone;
   * teardown "Why Are the V2.6 Files Half the Size of V2.5?": experts are
     stored as MXFP4, the router is BF16;
   * vLLM recipe "Overview": the arithmetic runs in block-scaled FP8 e4m3;
   * teardown "Why Are the V2.6 Files Half the Size of V2.5?", V2.5 column:
-    the earlier expert format, FP8 e4m3 with one float32 scale per 128 x 128
-    block (layer["format"] == "fp8_block").
+    the earlier expert format: e4m3 codes, each 128-row by 128-column tile with
+    its own float32 multiplier (layer["format"] == "fp8_block").
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes of the repository):
