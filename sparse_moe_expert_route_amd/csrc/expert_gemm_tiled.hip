@@ -182,7 +182,7 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
 // pointers: the compiler then tags every LDS access with the buffer it
 // touches, and its wait tracking for direct global->LDS loads lets a buffer
 // be read while the others are being filled.
-template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
+template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR, bool LDS_EPI = true>
 __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
                                            uint8_t* __restrict__ act2, uint8_t* __restrict__ act3,
                                            uint8_t* __restrict__ xsc, float* __restrict__ red,
@@ -452,7 +452,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         constexpr int NTT = decltype(nttc)::value;
         // ---- epilogue: lane holds tokens 32j + r and tile rows 8*(i/4) + 4g + (i%4) ----
         const int row0 = icur.row0, nrows = icur.nrows, nblk = icur.nblk;
-        if constexpr (MODE == kGemm2) {
+        if constexpr (MODE == kGemm2 && LDS_EPI) {
             // fp32 rows through a wave-private LDS tile, so that each store
             // instruction writes 8 whole 128-byte lines (8 lanes per row)
             // instead of 32-byte pieces of 32 lines: per (token tile j,
@@ -481,10 +481,27 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                         for (int u = 0; u < 2; ++u) {
                             const int row = 8 * u + (lane >> 3), ch = lane & 7;
                             const v4f v = *(const v4f*)(ot + row * kOutPitch + 4 * ch);
-                            if (32 * j + 16 * h + row < nrows) *(v4f*)(ob + (uint32_t)(row * a.H + 4 * ch)) = v;
+                            // whole lines, written once and not read again by this kernel: bypass the caches
+                            if (32 * j + 16 * h + row < nrows)
+                                __builtin_nontemporal_store(v, (v4f*)(ob + (uint32_t)(row * a.H + 4 * ch)));
                         }
                     }
                 }
+            }
+        } else if constexpr (MODE == kGemm2) {
+            // fp32 rows stored straight from the accumulators: lane (g, r)
+            // writes 16 bytes of row r per (tile, quarter), 32 rows per store
+#pragma unroll
+            for (int j = 0; j < NTT; ++j) {
+                if (r >= nrows - 32 * j) continue;
+                float* ob = (float*)a.out + ((size_t)(row0 + 32 * j) * a.H + nblk * kItemRows + 32 * kWT * wave);
+                const uint32_t lo = (uint32_t)(r * a.H + 4 * g);
+#pragma unroll
+                for (int t = 0; t < kWT; ++t)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *(v4f*)(ob + (lo + 32 * t + 8 * q)) =
+                            v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2], acc[t][j][4 * q + 3]};
             }
         } else if constexpr (MODE == kGemm1Preact) {
             // tile row 8q + 4g + i: q = 0, 1 gate features f + 8q + 4g + i, q = 2, 3 up
@@ -611,12 +628,16 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
 
 template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
 __global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmArgs a) {
-    // only the down GEMM's epilogue uses the output tile (its LDS is not
-    // allocated for the gate/up kernels)
-    if constexpr (MODE == kGemm2)
-        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, tl_out);
+    // The down GEMM's epilogue goes through the LDS output tile when the items
+    // are long (K of 1024 and more: Pro skewed prefill 2.05 -> 1.72 ms with the
+    // non-temporal stores); with two-stage items (K = 512, the tensor-parallel
+    // shares) the stores dominate and the detour costs more than it saves
+    // (1.113 ms direct against 1.215 ms).  Only kernels that use the tile
+    // have its LDS allocated.
+    if constexpr (MODE == kGemm2 && !PAIR)
+        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR, true>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, tl_out);
     else
-        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, nullptr);
+        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR, false>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, nullptr);
 }
 
 static int persistent_grid() {

@@ -66,9 +66,23 @@ __global__ void __launch_bounds__(512) perm_scan_kernel(const int32_t* __restric
     uint32_t bits = 0;
     for (int b = e; b < nblk; b += 512) bits |= block_err[b];
     if (bits) atomicOr(&err, bits);
+    // the exclusive prefix of expert e's column of block counts; sixteen loads
+    // of a column go out together (one chain of nblk dependent loads would
+    // cost a memory round trip per block: 36 us for 128 blocks)
     int run = 0;
     if (e < E) {
-        for (int b = 0; b < nblk; ++b) {
+        int b = 0;
+        for (; b + 16 <= nblk; b += 16) {
+            int c[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) c[u] = block_counts[(size_t)(b + u) * E + e];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                block_base[(size_t)(b + u) * E + e] = run;
+                run += c[u];
+            }
+        }
+        for (; b < nblk; ++b) {
             const int c = block_counts[(size_t)b * E + e];
             block_base[(size_t)b * E + e] = run;
             run += c;

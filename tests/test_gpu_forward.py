@@ -12,9 +12,11 @@ tie can legitimately route differently on the GPU (float32) and in the
 oracle (float64); they are excluded from the element-wise output comparison
 and their routing is checked for validity instead.  Likewise an h element
 whose exact value sits within the float32 accumulation error of an e4m3
-rounding midpoint has two correct codes; the oracle flags those and the
-output bar is widened by exactly one code step on each flagged element
-(tests/moe_testutil.py: h_rounding_allowance).
+rounding midpoint has two correct codes; the oracle flags those and, on the
+small layers, the output bar is widened by exactly one code step on each
+flagged element (tests/moe_testutil.py: h_rounding_allowance).  On the
+full-size workloads the plain bar max |y - y_ref| <= 2e-2 * RMS(y_ref) is
+asserted with no allowance.
 """
 
 import numpy as np
@@ -205,8 +207,7 @@ def test_forward_full_size_sampled(moe, cfg, packed, score):
         % (counts.max(), counts.mean(), counts.min(), (counts > 10 * counts.mean()).sum(), (counts > 0).sum()))
     # sampled tokens, evaluated by the oracle one by one
     rng = np.random.default_rng(1)
-    ns = 6 if T <= 128 else 3
-    toks = np.sort(rng.choice(T, size=min(ns, T), replace=False))
+    toks = np.sort(rng.choice(T, size=min(6, T), replace=False))
     log("  oracle on tokens %s" % toks.tolist())
     ref = oracle_with_allowance(lay, toks)
     tol = logit_tol(ref["logits"])
@@ -219,6 +220,8 @@ def test_forward_full_size_sampled(moe, cfg, packed, score):
     err, share = check_output(y[toks], ref, rows=clear)
     log("  max err / RMS = %.3e (%d of %d sampled tokens unambiguous); beyond the plain bar: %.2e"
         % (err, clear.sum(), len(toks), share))
+    # at full size no output element needs the rounding allowance: the plain bar holds
+    assert share == 0.0, "%.2e of the elements exceed 2e-2 x RMS" % share
 
 
 # ---------------------------------------------------------------------------
