@@ -80,20 +80,30 @@ struct F8Item {
     int e, row0, nrows, nblk;
 };
 
+// read-only data that every lane of a wave reads alike (constant address space)
+typedef const __attribute__((address_space(4))) int* cint_p;
+__device__ __forceinline__ int4 load_uniform4(const int4* p) {
+    const cint_p q = (cint_p)p;
+    return make_int4(q[0], q[1], q[2], q[3]);
+}
+
 __device__ __forceinline__ F8Item f8_item_at(const GemmArgs& a, int item, int NB) {
     // items of expert e: [NB * t0, NB * (t0 + nt)) with t0 its first tile in
     // the plan and nt = ceil(n_e / 128) its tiles; its m-tiles in chunks of
     // kF8MChunk, n-block major, m-tile minor within a chunk
-    const int4 head = a.tile_info[item / NB];
+    // (the plan and the offsets are read-only here and alike in every lane:
+    // scalar loads, which do not queue behind the wave's vector loads)
+    const cint_p offs = (cint_p)a.offsets;
+    const int4 head = load_uniform4(a.tile_info + item / NB);
     const int e = head.x, t0 = head.w;
-    const int nt = (a.offsets[e + 1] - a.offsets[e] + kF8TileRows - 1) / kF8TileRows;
+    const int nt = (offs[e + 1] - offs[e] + kF8TileRows - 1) / kF8TileRows;
     const int local = item - NB * t0;
     const int full = nt / kF8MChunk;
     const int chunk = min(local / (kF8MChunk * NB), full);
     const int cs = (chunk < full) ? kF8MChunk : nt - kF8MChunk * full;
     const int within = local - kF8MChunk * NB * chunk;
     const int nblk = within / cs;
-    const int4 ti = a.tile_info[t0 + kF8MChunk * chunk + (within - nblk * cs)];
+    const int4 ti = load_uniform4(a.tile_info + t0 + kF8MChunk * chunk + (within - nblk * cs));
     return F8Item{e, ti.y, ti.z, nblk};
 }
 
@@ -219,9 +229,11 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
 
         // One stage: for each of its two 128-deep blocks b and token tiles j,
         // two MFMAs into a fresh partial, then acc += partial * (weight scale x
-        // token scale).  The scheduling barriers keep the compiler from
-        // hoisting every LDS read (which costs registers the weights need);
-        // the two waves of a SIMD cover each other's LDS and MFMA latency.
+        // token scale).  Two partials alternate between the token tiles: the
+        // MFMAs of tile j run on the matrix core while the vector ALU scales
+        // and adds the partial of tile j - 1 (half of it after each MFMA).
+        // The scheduling barriers fix that order and keep the compiler from
+        // hoisting every LDS read (which costs registers the weights need).
         auto compute = [&](int st, int buf) __attribute__((always_inline)) {
             const uint8_t* lds = f8_lds.act[buf];
             const float* xsl = f8_lds.xsc[buf];
@@ -233,6 +245,14 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
                 const float wg = f8_lds.wsc[wave][0][2 * st + b], wu = f8_lds.wsc[wave][1][2 * st + b];
                 const v8i A0 = cat8(wreg[2 * b][0], wreg[2 * b][1]);
                 const v8i A1 = cat8(wreg[2 * b + 1][0], wreg[2 * b + 1][1]);
+                v16f part[2];
+                float cg[2], cu[2];
+                // elements 8h .. 8h + 7 of tile j's partial (h = 0: gate rows, 1: up rows)
+                auto rescale = [&](int j, int h) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int i = 8 * h; i < 8 * h + 8; ++i)
+                        acc[j][i] = __builtin_fmaf(part[j & 1][i], h == 0 ? cg[j & 1] : cu[j & 1], acc[j][i]);
+                };
 #pragma unroll
                 for (int j = 0; j < kF8TT; ++j) {
                     // steps 2b and 2b+1: chunks 4s + g and 4s + 2 + g of row 32j + r
@@ -241,15 +261,21 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
                     const v8i B0 = cat8(*(const v4i*)(rowp + slot[b][0]), *(const v4i*)(rowp + slot[b][1]));
                     const v8i B1 = cat8(*(const v4i*)(rowp + slot[b][2]), *(const v4i*)(rowp + slot[b][3]));
                     const float sx = xsl[2 * (32 * j + r) + b];
-                    v16f part = {};
-                    part = mfma32_f8f8(A0, B0, part);
-                    part = mfma32_f8f8(A1, B1, part);
+                    part[j & 1] = mfma32_f8f8(A0, B0, v16f{});
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (j > 0) rescale(j - 1, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    part[j & 1] = mfma32_f8f8(A1, B1, part[j & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (j > 0) rescale(j - 1, 1);
+                    cg[j & 1] = wg * sx;
+                    cu[j & 1] = wu * sx;
                     if (j == kF8TT - 1) load_w(wnext, b);   // block b's weights are no longer needed
-                    const float cg = wg * sx, cu = wu * sx;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[j][i] = __builtin_fmaf(part[i], i < 8 ? cg : cu, acc[j][i]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                rescale(kF8TT - 1, 0);
+                rescale(kF8TT - 1, 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 

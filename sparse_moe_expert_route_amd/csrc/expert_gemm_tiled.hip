@@ -74,6 +74,27 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
 __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_base, 4, 0, 0);
 }
+// The activation scale bytes of one stage for the four token tiles: bytes at
+// LDS offsets addr, addr + 128, addr + 256 and addr + 384, read in one asm
+// block that waits for its own reads.  The compiler's wait tracking for the
+// direct global->LDS loads cannot tell this copy from the activation ring
+// being filled, and before an ordinary read of it would wait for every load
+// in flight; the copy is complete and visible here through the stage's own
+// wait and barrier.
+__device__ __forceinline__ void lds_scale_bytes(uint32_t addr, uint32_t (&b)[4]) {
+    asm volatile(
+        "ds_read_u8 %0, %4\n\t"
+        "ds_read_u8 %1, %4 offset:128\n\t"
+        "ds_read_u8 %2, %4 offset:256\n\t"
+        "ds_read_u8 %3, %4 offset:384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(addr));
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kStageK + ((chunk ^ (row & 15)) << 4); }
 
 template <int OPSEL_A>
@@ -156,14 +177,25 @@ struct Rows {
     int xrow;              // row whose scale dwords the lane copies
 };
 
+// read-only data that every lane of a wave reads alike (constant address space)
+typedef const __attribute__((address_space(4))) int* cint_p;
+__device__ __forceinline__ int4 load_uniform4(const int4* p) {
+    const cint_p q = (cint_p)p;
+    return make_int4(q[0], q[1], q[2], q[3]);
+}
+
 __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
     // items of expert e: [NB * t0, NB * (t0 + nt)) with t0 its first tile in
     // the plan and nt = ceil(n_e / 128) its tiles.  Its m-tiles go in chunks of
     // kMChunk; within a chunk the order is n-block major, m-tile minor.  The
     // item multiplies the expert's token-tile class: its tiles' height / 32.
-    const int4 head = a.tile_info[item / NB];
+    // the plan and the offsets do not change during the kernel, and every lane
+    // reads the same entries: scalar loads, which neither wait behind the
+    // wave's vector loads in flight nor count against them
+    const cint_p offs = (cint_p)a.offsets;
+    const int4 head = load_uniform4(a.tile_info + item / NB);
     const int e = head.x, t0 = head.w;
-    const int ne = a.offsets[e + 1] - a.offsets[e];
+    const int ne = offs[e + 1] - offs[e];
     const int nt = (ne + kTileRows - 1) / kTileRows;
     const int local = item - NB * t0;
     const int full = nt / kMChunk;
@@ -171,7 +203,7 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
     const int cs = (chunk < full) ? kMChunk : nt - kMChunk * full;
     const int within = local - kMChunk * NB * chunk;
     const int nblk = within / cs;
-    const int4 ti = a.tile_info[t0 + kMChunk * chunk + (within - nblk * cs)];
+    const int4 ti = load_uniform4(a.tile_info + t0 + kMChunk * chunk + (within - nblk * cs));
     // every lane computes the same item: keep it in scalar registers
     return Item{__builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(ti.y),
                 __builtin_amdgcn_readfirstlane(ti.z), __builtin_amdgcn_readfirstlane(nblk),
@@ -343,9 +375,6 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         const uint8_t* xs = xsc + xpar * kXscBytes;
         // activation scale byte of each token tile (128-channel block 2st + g)
         const int xb = 2 * st + g;
-        int bs[NTT];
-#pragma unroll
-        for (int j = 0; j < NTT; ++j) bs[j] = xs[4 * ((xb >> 2) * kTileRows + 32 * j + r) + (xb & 3)];
         v8i B[NTT];
         auto read_b = [&](int j, int s) {
             const int row = 32 * j + r;
@@ -356,6 +385,13 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         };
 #pragma unroll
         for (int j = 0; j < NTT; ++j) read_b(j, 0);
+        int bs[NTT];
+        {
+            uint32_t b4[kTT];
+            lds_scale_bytes(lds_offset(xs) + 4 * ((xb >> 2) * kTileRows + r) + (xb & 3), b4);
+#pragma unroll
+            for (int j = 0; j < NTT; ++j) bs[j] = (int)b4[j];
+        }
         if constexpr (KIND == 1) lookup_rows(inxt, nxt);
         if constexpr (KIND == 2) dma_xsc(nxt.xrow, xsc + (xpar ^ 1) * kXscBytes);
         // prefetch targets: weights of the next stage, activations DA stages
