@@ -141,9 +141,11 @@ __global__ void __launch_bounds__(256) router_quant_kernel(const uint16_t* __res
 // experts (1 x 2 MFMA tiles).  K is walked in stages of 64 (128 bytes of a
 // bf16 row); each stage's 64 x rows and 128 W_r rows (24 KB) are copied by
 // direct global->LDS loads into a three-buffer ring, two stages ahead of
-// their use, with the 16-byte chunk c
-// of row p stored at slot c ^ (p mod 8) so that the 32 rows of one operand
-// fetch hit distinct banks.  Both operands use the same lane -> k mapping
+// their use, with the 16-byte chunk c of row p stored at slot
+// c ^ ((p / 2) mod 8): LDS serves a 16-byte read 16 lanes at a time across
+// 64 banks (256 bytes), and two 128-byte rows share one such window, so the
+// row's parity picks the half and (p / 2) mod 8 spreads the 8 rows of each
+// parity over the 8 slots; the 16 rows of a phase then hit distinct banks.  Both operands use the same lane -> k mapping
 // (8 consecutive k per lane), which is all a dot product needs.  Rows past T
 // or E are clamped for loading and not stored.  H % 64 == 0.
 // ---------------------------------------------------------------------------
@@ -161,7 +163,7 @@ __shared__ __attribute__((aligned(16))) uint8_t rt_buf0[kRtBuf];
 __shared__ __attribute__((aligned(16))) uint8_t rt_buf1[kRtBuf];
 __shared__ __attribute__((aligned(16))) uint8_t rt_buf2[kRtBuf];
 
-__device__ __forceinline__ int rt_swz(int row, int chunk) { return row * kRtRowBytes + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int rt_swz(int row, int chunk) { return row * kRtRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 __device__ __forceinline__ constexpr int rt_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // The K loop; the three LDS buffers come in as restrict pointers so that the
@@ -186,7 +188,7 @@ __device__ __forceinline__ void router_tiled_kloop(const uint16_t* __restrict__ 
 #pragma unroll
         for (int p = 0; p < kRtLoads; ++p) {
             const int row = 8 * kRtLoads * wave + 8 * p + (lane >> 3);    // 0..191
-            const int chunk = (lane & 7) ^ (row & 7);
+            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
             const uint16_t* src = (row < kRtTok) ? x + (size_t)min(t0 + row, T - 1) * H
                                                  : wr + (size_t)min(e0 + row - kRtTok, E - 1) * H;
             __builtin_amdgcn_global_load_lds(src + st * kRtStageK + 8 * chunk,
