@@ -51,7 +51,7 @@ extern "C" {
 /* Same declaration as the HIP runtime's: a stream handle is an opaque pointer. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
     MOE_OK = 0,
@@ -199,6 +199,24 @@ moe_status moe_prepack_weights(const moe_problem* problem, const moe_expert_weig
 moe_status moe_route(const moe_problem* problem, const void* x_bf16, const void* w_router_bf16,
                      const float* sel_bias, float* logits, int32_t* topk_ids, float* topk_w,
                      hipStream_t stream);
+
+/* One step of the rule that keeps the load spread over the experts through
+ * the selection bias (teardown, "How Big Is Each Expert?": the sigmoid
+ * scores get a small per-expert correction bias that evens out the load
+ * without an extra training loss; the page gives no update formula).  With
+ * n_e = expert_offsets[e+1] - expert_offsets[e] (the rows moe_permute gave
+ * expert e) and N = expert_offsets[E] - expert_offsets[0]:
+ *   sel_bias[e] += step   if E * n_e < N  (below the mean load),
+ *   sel_bias[e] -= step   if E * n_e > N  (above it),
+ *   unchanged             if E * n_e == N,
+ * the comparison exact (64-bit integers), the update one fp32 addition.
+ *   expert_offsets [E+1]  int32 device, as written by moe_permute
+ *   step                  fp32, finite (the caller's step size, e.g. 1e-3)
+ *   sel_bias       [E]    fp32 device, updated in place; 16-byte aligned
+ * Returns MOE_ERR_INVALID_ARGUMENT for a NULL pointer, a misaligned bias or
+ * a non-finite step.  Enqueued on `stream`, not waited for.               */
+moe_status moe_update_selection_bias(const moe_problem* problem, const int32_t* expert_offsets, float step,
+                                     float* sel_bias, hipStream_t stream);
 
 /* Permutation of the T*k routing slots by expert, and the FP8 activations in
  * expert order.  Slots are s = t*k + j.  Rows of one expert keep ascending

@@ -23,6 +23,9 @@ design notes of the repository):
     sigmoid scores over their sum; the selection key may carry an additive
     per-expert bias that does not enter the weights;
   * ties in the selection key go to the lower expert id, -0 equals +0;
+  * the load-balancing rule of the selection bias (no formula on the page):
+    after a batch an expert below the mean load gains +step, one above it
+    loses step (``update_selection_bias``);
   * the expert is SwiGLU: h = silu(gate) * up, silu(z) = z / (1 + exp(-z));
   * W13 stores the I gate rows first, then the I up rows;
   * activations and h are quantised with one power-of-two (e8m0) scale per
@@ -144,6 +147,36 @@ def select_topk(logits, k, bias=None, score="softmax"):
         z = np.take_along_axis(s64, ids, axis=1)
     w = z / z.sum(axis=1, keepdims=True)
     return ids, w
+
+
+def update_selection_bias(expert_offsets, step, bias):
+    """One step of the load-balancing rule for the selection bias.
+
+    Teardown "How Big Is Each Expert?": a small per-expert correction bias
+    on the sigmoid scores keeps the load across experts even, with no extra
+    training loss.  The page gives no update formula; the reading used here
+    is the plainest one that evens out the load: after a batch, an expert
+    that received fewer rows than the mean load N / E has its bias raised by
+    step, one that received more has it lowered by step, and one exactly at
+    the mean keeps it.  The comparison is exact (E * n_e against N as
+    integers); the new bias is one float32 addition b + (+-step).
+
+    expert_offsets: [E + 1] ints, the rows of expert e are
+        [expert_offsets[e], expert_offsets[e + 1])
+    step: the step size (a float32 value)
+    bias: [E] float32
+    returns the new bias, [E] float32
+    """
+    off = np.asarray(expert_offsets, dtype=np.int64)
+    E = off.size - 1
+    if E < 1:
+        raise ValueError("need at least one expert")
+    n = off[1:] - off[:-1]
+    total = off[-1] - off[0]
+    direction = np.sign(total - E * n)            # +1 below the mean load, -1 above
+    step32 = np.float32(step)
+    delta = np.where(direction > 0, step32, np.where(direction < 0, -step32, np.float32(0.0))).astype(np.float32)
+    return (np.asarray(bias, dtype=np.float32) + delta).astype(np.float32)
 
 
 def permutation(ids, num_experts):

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "MoeError", "Problem", "ExpertWeights", "lib_path", "load", "abi_version", "workspace_size",
     "alloc_workspace", "prepack_weights", "route", "permute", "grouped_gemm_swiglu", "grouped_gemm1_swiglu",
-    "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "forward_noalloc", "OUT_F32", "OUT_BF16",
+    "grouped_gemm1_preact", "grouped_gemm2", "combine", "forward", "forward_noalloc", "update_selection_bias",
+    "OUT_F32", "OUT_BF16",
     "WEIGHTS_CANONICAL", "WEIGHTS_PACKED", "EXPERTS_MXFP4", "EXPERTS_FP8_BLOCK", "EXPORTED_SYMBOLS",
     "scale_dtype", "error_words", "DEVERR_EXPERT_ID_RANGE", "DEVERR_EXPERT_ID_DUPLICATE", "DEVERR_EXPERT_OFFSETS",
 ]
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = [
     "moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_error_words_offset", "moe_prepack_weights",
     "moe_route", "moe_permute",
     "moe_grouped_gemm_swiglu", "moe_grouped_gemm1_swiglu", "moe_grouped_gemm1_preact",
-    "moe_grouped_gemm2", "moe_combine", "moe_forward", "moe_forward_noalloc",
+    "moe_grouped_gemm2", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_update_selection_bias",
 ]
 
 
@@ -236,6 +237,17 @@ def route(p, x, w_router, sel_bias, logits, topk_ids, topk_w, stream=None):
     st = load().moe_route(ctypes.byref(p), _ptr(x), _ptr(w_router), _ptr(sel_bias), _ptr(logits),
                           _ptr(topk_ids), _ptr(topk_w), _stream(stream))
     _raise("moe_route", st)
+
+
+def update_selection_bias(p, expert_offsets, step, sel_bias, stream=None):
+    """One load-balancing step of the selection bias, in place (moe_update_selection_bias):
+    experts below the mean load N / E get +step, those above it -step."""
+    E = p.num_experts
+    _check(expert_offsets, torch.int32, (E + 1,), "expert_offsets")
+    _check(sel_bias, torch.float32, (E,), "sel_bias")
+    st = load().moe_update_selection_bias(ctypes.byref(p), _ptr(expert_offsets), ctypes.c_float(step), _ptr(sel_bias),
+                                          _stream(stream))
+    _raise("moe_update_selection_bias", st)
 
 
 def permute(p, topk_ids, x, expert_offsets, sorted_token, row_of_slot, xq_perm, xs_perm, ws, stream=None):

@@ -5,6 +5,8 @@
 // the first launch, so a rejected call enqueues nothing.
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
+
 #include "moe.h"
 #include "moe_launch.h"
 
@@ -391,6 +393,14 @@ moe_status moe_grouped_gemm_swiglu(const moe_problem* p, const uint8_t* xq_perm,
     void* hs = at<uint8_t>(ws, L.hs);
     MOE_CHECK(run_gemm1(*p, kGemm1Swiglu, xq_perm, xs_perm, expert_offsets, *weights, hq, hs, ws, true, stream));
     return run_gemm2(*p, hq, hs, expert_offsets, *weights, y_perm, ws, false, stream);
+}
+
+moe_status moe_update_selection_bias(const moe_problem* p, const int32_t* expert_offsets, float step, float* sel_bias,
+                                     hipStream_t stream) {
+    MOE_CHECK(check_problem(p));
+    if (!expert_offsets || !all_aligned(sel_bias) || !std::isfinite(step)) return MOE_ERR_INVALID_ARGUMENT;
+    MOE_LAUNCH(launch_bias_update(expert_offsets, p->num_experts, step, sel_bias, stream));
+    return MOE_OK;
 }
 
 moe_status moe_combine(const moe_problem* p, const float* y_perm, const int32_t* row_of_slot, const float* topk_w,

@@ -32,6 +32,8 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, flo
                                 int64_t T, int H, int E, hipStream_t stream);
 hipError_t launch_topk(const float* logits, const float* bias, int32_t* ids, float* w, int64_t T, int E,
                        int k, int sigmoid, hipStream_t stream);
+// One step of the selection-bias load-balancing rule (moe_update_selection_bias).
+hipError_t launch_bias_update(const int32_t* offsets, int E, float step, float* bias, hipStream_t stream);
 // Up to kDecodeRouterMaxT tokens the router runs its decode kernel; there it
 // can also write the token-order FP8 copy of x (xq [T][H], xs [T][H/128]) in
 // the same launch.

@@ -297,6 +297,28 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, flo
 }
 
 // ---------------------------------------------------------------------------
+// Selection-bias load balancing, one step (the rule of
+// moe_update_selection_bias): an expert below the mean load N / E gets
+// +step, one above it -step; E * n_e against N in 64-bit integers, so the
+// sign is exact; the new bias is one fp32 addition.  One thread per expert.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bias_update_kernel(const int32_t* __restrict__ offsets, int E, float step,
+                                                          float* __restrict__ bias) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    const int64_t n = (int64_t)offsets[e + 1] - offsets[e];
+    const int64_t N = (int64_t)offsets[E] - offsets[0];
+    const int64_t d = N - (int64_t)E * n;
+    const float delta = d > 0 ? step : (d < 0 ? -step : 0.0f);
+    bias[e] = bias[e] + delta;
+}
+
+hipError_t launch_bias_update(const int32_t* offsets, int E, float step, float* bias, hipStream_t stream) {
+    hipLaunchKernelGGL(bias_update_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, offsets, E, step, bias);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Top-k selection + softmax weights: one wave per token.
 //
 // key = fp32(L + b).  Each key is mapped to an unsigned integer that orders

@@ -82,6 +82,12 @@ hipError_t launch_topk(const float* logits, const float*, int32_t* ids, float* w
     return hipSuccess;
 }
 
+hipError_t launch_bias_update(const int32_t* off, int E, float, float* bias, hipStream_t) {
+    need(off && bias && E >= 1 && E <= 512, "launch_bias_update", "arguments");
+    count("launch_bias_update");
+    return hipSuccess;
+}
+
 hipError_t launch_router_quant(const uint16_t* x, const uint16_t* w, float* logits, int64_t T, int H, int E,
                                uint8_t* xq, void* xs, int, hipStream_t) {
     need(x && w && logits && xq && xs && T >= 1 && T <= kDecodeRouterMaxT && H >= 128 && E >= 1,

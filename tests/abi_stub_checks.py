@@ -39,7 +39,7 @@ def _w(fmt_layout=0):
 NAMES = ["launch_router_logits", "launch_router_quant", "launch_topk", "launch_perm_small", "launch_perm_count",
          "launch_perm_scan", "launch_perm_scatter", "launch_quant_gather", "launch_tile_plan", "launch_expert_gemm",
          "launch_expert_gemm_tiled", "launch_expert_gemm_fp8", "launch_expert_gemm_fp8_tiled", "launch_combine",
-         "launch_prepack", "launch_prepack_scales", "hipMemcpyAsync"]
+         "launch_prepack", "launch_prepack_scales", "launch_bias_update", "hipMemcpyAsync"]
 
 
 def _delta(lib, fn):
@@ -107,6 +107,7 @@ def test_staged_entry_points(lib, T, H, I, E, k):
                                              None),
         lambda: lib.moe_grouped_gemm2(ctypes.byref(p), vp(A), vp(A), vp(A), ctypes.byref(w), vp(A), vp(A), ws, None),
         lambda: lib.moe_combine(ctypes.byref(p), vp(A), vp(A), vp(A), vp(A), 1, None),
+        lambda: lib.moe_update_selection_bias(ctypes.byref(p), vp(A), ctypes.c_float(0.001), vp(A), None),
     ]
     for c in calls:
         assert c() == 0
@@ -140,3 +141,13 @@ def test_forward_noalloc_runs_the_forward_in_the_scratch_array(lib, T, H, I, E, 
     st, d = _delta(lib, lambda: lib.moe_forward_noalloc(ctypes.byref(p), vp(A), vp(A), None, ctypes.byref(w), vp(A),
                                                         0, None))
     assert st == 0 and d == d_ref
+
+
+@pytest.mark.parametrize("E", [1, 256, 512])
+def test_selection_bias_update_launches_once(lib, E):
+    p = moe.Problem.make(64, 256, 128, E, 1, 1)
+    vp = ctypes.c_void_p
+    st, d = _delta(lib, lambda: lib.moe_update_selection_bias(ctypes.byref(p), vp(A), ctypes.c_float(0.5), vp(A),
+                                                              None))
+    assert st == 0
+    assert d == {"launch_bias_update": 1}

@@ -50,7 +50,7 @@ def test_micro_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings(lib):
-    assert moe.abi_version() == 5
+    assert moe.abi_version() == 6
     for st, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"), (4, b"HIP launch failure")]:
         assert lib.moe_status_string(st) == text
     assert lib.moe_status_string(99) == b"unknown status"
@@ -137,6 +137,14 @@ def test_invalid_arguments_rejected_before_launch(lib):
     p8 = _P(fmt=1)
     assert prepack(p8, w, [vp(FAKE + 384 * 1024)] + outs[1:]) == 1   # inside the e4m3 w13 input
     assert prepack(p8, wp, outs) == 1
+    # selection-bias update: null offsets, misaligned or null bias, non-finite step
+    f = ctypes.c_float
+    assert lib.moe_update_selection_bias(ctypes.byref(p), None, f(0.01), vp(FAKE), None) == 1
+    assert lib.moe_update_selection_bias(ctypes.byref(p), vp(FAKE), f(0.01), vp(FAKE + 4), None) == 1
+    assert lib.moe_update_selection_bias(ctypes.byref(p), vp(FAKE), f(0.01), None, None) == 1
+    assert lib.moe_update_selection_bias(ctypes.byref(p), vp(FAKE), f(float("nan")), vp(FAKE), None) == 1
+    assert lib.moe_update_selection_bias(ctypes.byref(p), vp(FAKE), f(float("inf")), vp(FAKE), None) == 1
+    assert lib.moe_update_selection_bias(ctypes.byref(pb), vp(FAKE), f(0.01), vp(FAKE), None) == 1
     # unknown scoring function
     ps = _P(sf=2)
     assert lib.moe_route(ctypes.byref(ps), None, None, None, vp(FAKE), vp(FAKE), vp(FAKE), None) == 2
