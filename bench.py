@@ -65,6 +65,11 @@ def parse():
                     help="run on the canonical (row-major) weight layout instead of the packed one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB copy kernel (for scaling HBM byte counters)")
+    ap.add_argument("--power", action="store_true",
+                    help="sample the board power and graphics clock (amd-smi) while the workload's gate/up GEMM, "
+                         "down GEMM and whole forward, and the FP4 x FP8 MFMA microbenchmark, each run back to back "
+                         "for --power-seconds; print their JSON line")
+    ap.add_argument("--power-seconds", type=float, default=5.0)
     ap.add_argument("--micro", action="store_true",
                     help="run the microbenchmarks of the HBM and MFMA ceilings (include/moe_micro.h) instead, "
                          "and print their JSON line")
@@ -114,6 +119,9 @@ def main():
         sys.exit(2)
     if args.micro:
         print(json.dumps(micro()), flush=True)
+        return
+    if args.power:
+        print(json.dumps(power(args)), flush=True)
         return
     import numpy as np
     import torch
@@ -320,6 +328,126 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(lay, args, T)
     print(json.dumps(out), flush=True)
+
+
+def _smi_sample():
+    """(socket power W, mean graphics clock MHz over the XCDs) from amd-smi, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=5)
+        d = json.loads(r.stdout)["gpu_data"][0]
+        clk = [v["clk"]["value"] for k_, v in d["clock"].items() if k_.startswith("gfx")]
+        return float(d["power"]["socket_power"]["value"]), float(sum(clk) / len(clk))
+    except Exception:
+        return None
+
+
+def power(args):
+    """Board power and graphics clock while each of the workload's GEMMs, its whole forward and
+    the FP4 x FP8 MFMA microbenchmark (register operands, no memory traffic) run back to back:
+    a sampling thread polls amd-smi about every 0.1 s; each phase reports the medians of the
+    samples taken inside it (its first 0.5 s left out) and its time per call."""
+    import ctypes
+    import threading
+    import numpy as np
+    import torch
+    import sparse_moe_expert_route_amd as moe
+    from sparse_moe_expert_route_amd import build as B
+    import synthetic as S
+
+    if _smi_sample() is None:
+        raise RuntimeError("amd-smi is not available")
+    cfg = S.config(args.config)
+    T, H, E, k, inter = cfg["T"], cfg["H"], cfg["E"], cfg["k"], cfg["I"]
+    fp8 = cfg["format"] == "fp8_block"
+    N = T * k
+    lay = S.make_layer(args.config, seed=args.seed)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wr = dev(lay["x"]), dev(lay["w_router"])
+    bias = None if lay["bias"] is None else dev(lay["bias"])
+    p = moe.Problem.make(T, H, inter, E, k, 0, moe.EXPERTS_FP8_BLOCK if fp8 else moe.EXPERTS_MXFP4)
+    W = moe.prepack_weights(p, moe.ExpertWeights(dev(lay["w13"]), dev(lay["w13_s"]), dev(lay["w2"]), dev(lay["w2_s"])))
+    del lay
+    ws = moe.alloc_workspace(p)
+    sd = moe.scale_dtype(p)
+    L = torch.empty(T, E, device="cuda")
+    ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    st = torch.empty(N, dtype=torch.int32, device="cuda")
+    ros = torch.empty(N, dtype=torch.int32, device="cuda")
+    xq = torch.empty(N, H, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(N, H // 128, dtype=sd, device="cuda")
+    hq = torch.empty(N, inter, dtype=torch.uint8, device="cuda")
+    hs = torch.empty(N, inter // 128, dtype=sd, device="cuda")
+    yp = torch.empty(N, H, device="cuda")
+    y = torch.empty(T, H, device="cuda")
+    moe.route(p, x, wr, bias, L, ids, w)
+    moe.permute(p, ids, x, off, st, ros, xq, xs, ws)
+    moe.grouped_gemm1_swiglu(p, xq, xs, off, W, hq, hs, ws)
+    torch.cuda.synchronize()
+
+    micro_lib = ctypes.CDLL(B.MICRO_LIB)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    micro_lib.moe_micro_mfma.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fo = torch.empty(cus * 2 * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sp = vp(torch.cuda.current_stream().cuda_stream)
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            s_ = _smi_sample()
+            if s_ is not None:
+                samples.append((time.time(),) + s_)
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(1.0)
+    idle = [s_ for s_ in samples]
+    phases = [
+        ("gemm1_swiglu", lambda: moe.grouped_gemm1_swiglu(p, xq, xs, off, W, hq, hs, ws)),
+        ("gemm2", lambda: moe.grouped_gemm2(p, hq, hs, off, W, yp, ws)),
+        ("forward", lambda: moe.forward(p, x, wr, bias, W, y, ws)),
+        ("mfma_microbenchmark_32x32x64_fp4xfp8",
+         lambda: micro_lib.moe_micro_mfma(4, 0, 32, 4096, cus * 2, vp(fo.data_ptr()), vp(clk.data_ptr()), sp)),
+    ]
+    out = {"workload": args.config, "idle_W": round(float(np.median([s_[1] for s_ in idle])), 1) if idle else None,
+           "phases": {}}
+    for name, fn in phases:
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        while time.time() - t0 < args.power_seconds:
+            for _ in range(4):
+                fn()
+                n += 1
+            torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        inside = [s_ for s_ in samples if t0 + 0.5 < s_[0] < t1]
+        out["phases"][name] = {
+            "ms_per_call": round(e0.elapsed_time(e1) / n, 4),
+            "samples": len(inside),
+            "power_W_median": round(float(np.median([s_[1] for s_ in inside])), 1) if inside else None,
+            "gfx_clock_MHz_median": round(float(np.median([s_[2] for s_ in inside])), 1) if inside else None,
+        }
+        log("power: %s %s" % (name, out["phases"][name]))
+        time.sleep(1.0)
+    stop.set()
+    th.join(timeout=10)
+    return {"power": out}
 
 
 def micro():
