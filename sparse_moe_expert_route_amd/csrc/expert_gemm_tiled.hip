@@ -189,9 +189,9 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
     // the plan and nt = ceil(n_e / 128) its tiles.  Its m-tiles go in chunks of
     // kMChunk; within a chunk the order is n-block major, m-tile minor.  The
     // item multiplies the expert's token-tile class: its tiles' height / 32.
-    // the plan and the offsets do not change during the kernel, and every lane
-    // reads the same entries: scalar loads, which neither wait behind the
-    // wave's vector loads in flight nor count against them
+    // The plan and the offsets do not change during the kernel and every lane
+    // reads the same entries, so they come through scalar loads, which neither
+    // wait behind the wave's vector loads in flight nor count against them.
     const cint_p offs = (cint_p)a.offsets;
     const int4 head = load_uniform4(a.tile_info + item / NB);
     const int e = head.x, t0 = head.w;
@@ -210,10 +210,11 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
                 __builtin_amdgcn_readfirstlane(tile_height(ne, nt) >> 5)};
 }
 
-// The persistent loop of one workgroup.  LDS buffers come in as restrict
-// pointers: the compiler then tags every LDS access with the buffer it
-// touches, and its wait tracking for direct global->LDS loads lets a buffer
-// be read while the others are being filled.
+// The persistent loop of one workgroup.  The LDS buffers are separate
+// objects: the compiler's wait tracking for direct global->LDS loads tells
+// accesses to different objects apart, so a ring buffer can be read while the
+// others are being filled (the scale copy, one object of two halves, is read
+// in asm for that reason).
 template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR, bool LDS_EPI = true>
 __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
                                            uint8_t* __restrict__ act2, uint8_t* __restrict__ act3,

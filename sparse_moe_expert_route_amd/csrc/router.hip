@@ -166,8 +166,8 @@ __shared__ __attribute__((aligned(16))) uint8_t rt_buf2[kRtBuf];
 __device__ __forceinline__ int rt_swz(int row, int chunk) { return row * kRtRowBytes + ((chunk ^ ((row >> 1) & 7)) << 4); }
 __device__ __forceinline__ constexpr int rt_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// The K loop; the three LDS buffers come in as restrict pointers so that the
-// compiler's wait tracking for direct-to-LDS loads tells them apart.
+// The K loop; the three LDS buffers are separate objects, which the
+// compiler's wait tracking for direct-to-LDS loads tells apart.
 __device__ __forceinline__ void router_tiled_kloop(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
                                                    int T, int H, int E, int t0, int e0, v16f_r (&acc)[2],
                                                    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1,
