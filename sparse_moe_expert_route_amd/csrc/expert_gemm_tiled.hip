@@ -118,9 +118,11 @@ constexpr int kXscLoads = (kMaxK / kFp8Block / 2 + kWaves - 1) / kWaves;
 __shared__ __attribute__((aligned(16))) uint8_t tl_xsc[2 * kXscBytes];
 // per-row maxima of the SwiGLU epilogue
 __shared__ float tl_red[kWaves * kTileRows];
-// down-GEMM epilogue: one 16-row x 32-feature fp32 tile per wave (rows padded
-// to 36 floats so the 16-byte writes of a row's two lane halves and the
-// row-order reads spread over the banks)
+// down-GEMM epilogue: one 16-row x 32-feature fp32 tile per wave, rows padded
+// to 36 floats.  LDS serves a 16-byte access 16 lanes at a time across 64
+// banks: the writes (one 16-byte chunk of each of the 16 rows) then hit 16
+// distinct banks, and so do the reads, whose 16 lanes take the 8 chunks of
+// rows p and p + 8 (nine bank groups per row apart, 72 = 8 mod 16).
 constexpr int kOutPitch = 36;
 __shared__ __attribute__((aligned(16))) float tl_out[kWaves * 16 * kOutPitch];
 
@@ -516,7 +518,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                                                      32 * kWT * wave + 32 * t);
 #pragma unroll
                         for (int u = 0; u < 2; ++u) {
-                            const int row = 8 * u + (lane >> 3), ch = lane & 7;
+                            const int row = 8 * ((lane >> 3) & 1) + (lane >> 4) + 4 * u, ch = lane & 7;
                             const v4f v = *(const v4f*)(ot + row * kOutPitch + 4 * ch);
                             // whole lines, written once and not read again by this kernel: bypass the caches
                             if (32 * j + 16 * h + row < nrows)
