@@ -1,6 +1,7 @@
 // Grouped expert GEMMs for shapes with many rows per expert (prefill):
 // LDS-tiled, on the 32x32x64 block-scaled MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4), A = MXFP4 weights, B = FP8 activations.
+// (v_mfma_scale_f32_32x32x64_f8f6f4), A = MXFP4 weights, B = FP8 activations
+// (the other way round in the down GEMM of items of four or more stages).
 //
 // Same computation as the streaming kernel (expert_gemm.hip): experts are
 // gate, up and down matrices with an intermediate width of 2,048 (teardown,
@@ -101,6 +102,14 @@ template <int OPSEL_A>
 __device__ __forceinline__ v16f mfma32_w4a8(v8i a, v8i b, v16f c, int scale_a, int scale_b) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 0, OPSEL_A, scale_a, 0, scale_b);
 }
+// The same product with the operands in the other order (FP8 activations as
+// A, MXFP4 weights as B; the register contents of both are unchanged): the
+// accumulators then hold D transposed, acc[i] of lane l being token
+// 8*(i/4) + 4g + (i%4) of the token tile and feature r of the weight tile.
+template <int OPSEL_B>
+__device__ __forceinline__ v16f mfma32_a8w4(v8i act, v8i w, v16f c, int scale_act, int scale_w) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(act, w, c, 0, 4, 0, scale_act, OPSEL_B, scale_w);
+}
 
 // Activation stage ring in LDS: four buffers, declared as separate objects
 // so that the compiler's wait tracking for direct global->LDS loads can tell
@@ -118,13 +127,6 @@ constexpr int kXscLoads = (kMaxK / kFp8Block / 2 + kWaves - 1) / kWaves;
 __shared__ __attribute__((aligned(16))) uint8_t tl_xsc[2 * kXscBytes];
 // per-row maxima of the SwiGLU epilogue
 __shared__ float tl_red[kWaves * kTileRows];
-// down-GEMM epilogue: one 16-row x 32-feature fp32 tile per wave, rows padded
-// to 36 floats.  LDS serves a 16-byte access 16 lanes at a time across 64
-// banks: the writes (one 16-byte chunk of each of the 16 rows) then hit 16
-// distinct banks, and so do the reads, whose 16 lanes take the 8 chunks of
-// rows p and p + 8 (nine bank groups per row apart, 72 = 8 mod 16).
-constexpr int kOutPitch = 36;
-__shared__ __attribute__((aligned(16))) float tl_out[kWaves * 16 * kOutPitch];
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9
 // encoding, vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
@@ -136,6 +138,7 @@ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // offset, so that the loads cost no per-load address registers.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit elements (gfx9 family)
+constexpr int kNonTemporal = 2;           // cache-policy bit of a buffer store: non-temporal
 __device__ __forceinline__ rsrc_t make_rsrc(const uint8_t* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, 0x7fffffff, kRsrcWord3);
 }
@@ -217,14 +220,21 @@ __device__ __forceinline__ Item item_at(const GemmArgs& a, int item, int NB) {
 // accesses to different objects apart, so a ring buffer can be read while the
 // others are being filled (the scale copy, one object of two halves, is read
 // in asm for that reason).
-template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR, bool LDS_EPI = true>
+template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
 __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restrict__ act0, uint8_t* __restrict__ act1,
                                            uint8_t* __restrict__ act2, uint8_t* __restrict__ act3,
-                                           uint8_t* __restrict__ xsc, float* __restrict__ red,
-                                           float* __restrict__ out_tile) {
+                                           uint8_t* __restrict__ xsc, float* __restrict__ red) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, r = lane & 31;
+    // Down GEMM, items of four or more stages: the operands go to the MFMA the
+    // other way round (same register contents, bit-identical results) so that
+    // the fp32 rows leave as whole lines straight from the accumulators (Pro
+    // skewed prefill 1.71 -> 1.67 ms against rows staged through an LDS
+    // tile).  Two-stage items (K = 512, the tensor-parallel shares) keep the
+    // weight-major order and store 32-byte pieces: the token-major epilogue
+    // spills about 110 registers there and took 1.16 -> 1.79 ms.
+    constexpr bool TOKEN_MAJOR = MODE == kGemm2 && !PAIR;
 
     const int K = (MODE == kGemm2) ? a.I : a.H;
     const int wrows = (MODE == kGemm2) ? a.H : 2 * a.I;
@@ -434,11 +444,21 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
                     const uint4 w = wreg[s][t];
                     const v8i A = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
                     const int sa = (int)wsc[SET][t];
-                    switch (s) {
-                        case 0: acc[t][j] = mfma32_w4a8<0>(A, B[j], acc[t][j], sa, bs[j]); break;
-                        case 1: acc[t][j] = mfma32_w4a8<1>(A, B[j], acc[t][j], sa, bs[j]); break;
-                        case 2: acc[t][j] = mfma32_w4a8<2>(A, B[j], acc[t][j], sa, bs[j]); break;
-                        default: acc[t][j] = mfma32_w4a8<3>(A, B[j], acc[t][j], sa, bs[j]); break;
+                    if constexpr (TOKEN_MAJOR) {
+                        // token-major accumulators for the down GEMM's fp32 stores
+                        switch (s) {
+                            case 0: acc[t][j] = mfma32_a8w4<0>(B[j], A, acc[t][j], bs[j], sa); break;
+                            case 1: acc[t][j] = mfma32_a8w4<1>(B[j], A, acc[t][j], bs[j], sa); break;
+                            case 2: acc[t][j] = mfma32_a8w4<2>(B[j], A, acc[t][j], bs[j], sa); break;
+                            default: acc[t][j] = mfma32_a8w4<3>(B[j], A, acc[t][j], bs[j], sa); break;
+                        }
+                    } else {
+                        switch (s) {
+                            case 0: acc[t][j] = mfma32_w4a8<0>(A, B[j], acc[t][j], sa, bs[j]); break;
+                            case 1: acc[t][j] = mfma32_w4a8<1>(A, B[j], acc[t][j], sa, bs[j]); break;
+                            case 2: acc[t][j] = mfma32_w4a8<2>(A, B[j], acc[t][j], sa, bs[j]); break;
+                            default: acc[t][j] = mfma32_w4a8<3>(A, B[j], acc[t][j], sa, bs[j]); break;
+                        }
                     }
                 }
                 if (s < 3) read_b(j, s + 1);
@@ -491,38 +511,36 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
         constexpr int NTT = decltype(nttc)::value;
         // ---- epilogue: lane holds tokens 32j + r and tile rows 8*(i/4) + 4g + (i%4) ----
         const int row0 = icur.row0, nrows = icur.nrows, nblk = icur.nblk;
-        if constexpr (MODE == kGemm2 && LDS_EPI) {
-            // fp32 rows through a wave-private LDS tile, so that each store
-            // instruction writes 8 whole 128-byte lines (8 lanes per row)
-            // instead of 32-byte pieces of 32 lines: per (token tile j,
-            // weight tile t) and half h of the 32 rows, the lanes holding rows
-            // 16h .. 16h+15 put their 16 features of the row into the tile,
-            // then every lane reads one 16-byte chunk of a row back.  LDS
-            // operations of one wave run in order, so no barrier is needed.
-            float* ot = out_tile + wave * (16 * kOutPitch);
+        if constexpr (TOKEN_MAJOR) {
+            // token-major accumulators (mfma32_a8w4): lane (g, r) holds feature
+            // r of weight tile t for token rows 8*(i/4) + 4g + (i%4) of token
+            // tile j, so one dword store over the wave writes two whole
+            // 128-byte lines (rows p and p + 4) straight from the registers.
+            // Written once and not read again by this kernel: the stores
+            // bypass the caches.  Buffer stores: the item's base in the
+            // resource, the lane's byte offset in one register, the row's in
+            // the scalar offset.  The row stride and the lane offset pass
+            // through an empty asm statement, so the 64 row offsets are derived
+            // here rather than kept live across the item loop.
+            const rsrc_t ro = make_rsrc((const uint8_t*)a.out +
+                                        4 * ((size_t)row0 * a.H + nblk * kItemRows + 32 * kWT * wave));
+            int hb = 4 * a.H;
+            uint32_t vo = 4 * (4 * g * a.H + r);
+            asm volatile("" : "+s"(hb), "+v"(vo));
 #pragma unroll
             for (int j = 0; j < NTT; ++j) {
                 if (32 * j >= nrows) break;   // token tiles past the item's rows hold nothing
 #pragma unroll
-                for (int t = 0; t < kWT; ++t) {
+                for (int i = 0; i < 16; ++i) {
+                    const int p = 32 * j + 8 * (i >> 2) + (i & 3);   // row of lanes 0..31; lanes 32..63: p + 4
+                    if (p + 4 * g < nrows) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        if ((r >> 4) == h) {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                *(v4f*)(ot + (r & 15) * kOutPitch + 8 * q + 4 * g) =
-                                    v4f{acc[t][j][4 * q], acc[t][j][4 * q + 1], acc[t][j][4 * q + 2], acc[t][j][4 * q + 3]};
-                        }
-                        // uniform base plus a 32-bit lane offset
-                        float* ob = (float*)a.out + ((size_t)(row0 + 32 * j + 16 * h) * a.H + nblk * kItemRows +
-                                                     32 * kWT * wave + 32 * t);
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int row = 8 * ((lane >> 3) & 1) + (lane >> 4) + 4 * u, ch = lane & 7;
-                            const v4f v = *(const v4f*)(ot + row * kOutPitch + 4 * ch);
-                            // whole lines, written once and not read again by this kernel: bypass the caches
-                            if (32 * j + 16 * h + row < nrows)
-                                __builtin_nontemporal_store(v, (v4f*)(ob + (uint32_t)(row * a.H + 4 * ch)));
+                        for (int t = 0; t < kWT; ++t) {
+                            // copied out first: this compiler's bit cast of a vector element
+                            // expression reads element 0 whatever the index
+                            const float v = acc[t][j][i];
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, vo + 128 * t,
+                                                                  p * hb, kNonTemporal);
                         }
                     }
                 }
@@ -667,16 +685,7 @@ __device__ __forceinline__ void tiled_gemm(const GemmArgs& a, uint8_t* __restric
 
 template <int MODE, bool PACKED, bool GATHER, int DA, bool PAIR>
 __global__ void __launch_bounds__(64 * kWaves, 1) expert_gemm_tiled_kernel(GemmArgs a) {
-    // The down GEMM's epilogue goes through the LDS output tile when the items
-    // are long (K of 1024 and more: Pro skewed prefill 2.05 -> 1.72 ms with the
-    // non-temporal stores); with two-stage items (K = 512, the tensor-parallel
-    // shares) the stores dominate and the detour costs more than it saves
-    // (1.113 ms direct against 1.215 ms).  Only kernels that use the tile
-    // have its LDS allocated.
-    if constexpr (MODE == kGemm2 && !PAIR)
-        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR, true>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, tl_out);
-    else
-        tiled_gemm<MODE, PACKED, GATHER, DA, PAIR, false>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red, nullptr);
+    tiled_gemm<MODE, PACKED, GATHER, DA, PAIR>(a, tl_act0, tl_act1, tl_act2, tl_act3, tl_xsc, tl_red);
 }
 
 static int persistent_grid() {
