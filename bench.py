@@ -553,19 +553,47 @@ def cpu_baseline(lay, args, T):
     except ImportError:   # pragma: no cover
         threadpool_info = threadpool_limits = None
     log("bench: CPU oracle on %d tokens, %d cores" % (n, cores))
-    t0 = time.perf_counter()
-    if threadpool_limits:
-        with threadpool_limits(limits=cores, user_api="blas"):
-            info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-            if info:
-                blas = {"vendor": "%s %s" % (info[0].get("internal_api"), info[0].get("version")),
-                        "threads": info[0].get("num_threads")}
+    # time split: the oracle's expert-weight decoding, its per-expert work (the
+    # decoding, both GEMMs, SwiGLU and the FP8 requantisation of h) and the rest
+    # (router logits, top-k, FP8 quantisation of x, combine), by timing wrappers
+    # around two of its functions for the length of this call (its arithmetic
+    # is untouched)
+    spent = {"decode": 0.0, "experts": 0.0}
+    orig = {"decode_expert_matrix": OL.decode_expert_matrix, "expert_ffn": OL.expert_ffn}
+
+    def timed(name, key):
+        f = orig[name]
+
+        def g(*a, **kw):
+            t = time.perf_counter()
+            try:
+                return f(*a, **kw)
+            finally:
+                spent[key] += time.perf_counter() - t
+        return g
+
+    OL.decode_expert_matrix = timed("decode_expert_matrix", "decode")
+    OL.expert_ffn = timed("expert_ffn", "experts")
+    try:
+        t0 = time.perf_counter()
+        if threadpool_limits:
+            with threadpool_limits(limits=cores, user_api="blas"):
+                info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+                if info:
+                    blas = {"vendor": "%s %s" % (info[0].get("internal_api"), info[0].get("version")),
+                            "threads": info[0].get("num_threads")}
+                OL.forward_tokens(lay, toks)
+        else:
             OL.forward_tokens(lay, toks)
-    else:
-        OL.forward_tokens(lay, toks)
-    sec = time.perf_counter() - t0
+        sec = time.perf_counter() - t0
+    finally:
+        OL.decode_expert_matrix = orig["decode_expert_matrix"]
+        OL.expert_ffn = orig["expert_ffn"]
+    split = {"expert_decode": round(spent["decode"], 3),
+             "expert_gemms_swiglu_requant": round(spent["experts"] - spent["decode"], 3),
+             "rest": round(sec - spent["experts"], 3)}
     return {"value": round(n / sec, 4), "unit": "tokens/s", "cores": blas["threads"] or cores, "kind": "oracle",
-            "cpu": _cpu_model(), "blas": blas["vendor"], "affinity_cores": cores,
+            "cpu": _cpu_model(), "blas": blas["vendor"], "affinity_cores": cores, "split_s": split,
             "sample": "first %d tokens of the %s workload, whole layer (router, routing, FP8 quantisation, all "
                       "their experts decoded from %s and run in float64 with BLAS on %s threads, combine); %.1f s"
                       % (n, args.config, "FP8 blocks" if lay.get("format") == "fp8_block" else "MXFP4",
