@@ -76,17 +76,18 @@ def parse():
     return ap.parse_args()
 
 
-# the sources the gate/up GEMM's HBM traffic depends on (kernels, shared headers, the tile plan)
-GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm.hip",
-                "sparse_moe_expert_route_amd/csrc/expert_gemm_tiled.hip",
-                "sparse_moe_expert_route_amd/csrc/moe_internal.h",
-                "sparse_moe_expert_route_amd/csrc/moe_launch.h",
-                "sparse_moe_expert_route_amd/csrc/permute.hip"]
-FP8_GEMM_SOURCES = ["sparse_moe_expert_route_amd/csrc/expert_gemm_fp8.hip",
-                    "sparse_moe_expert_route_amd/csrc/expert_gemm_fp8_tiled.hip",
-                    "sparse_moe_expert_route_amd/csrc/moe_internal.h",
-                    "sparse_moe_expert_route_amd/csrc/moe_launch.h",
-                    "sparse_moe_expert_route_amd/csrc/permute.hip"]
+# the sources the gate/up GEMM's HBM traffic depends on: the kernel that runs
+# (streaming on decode-sized batches, LDS-tiled on prefill-sized ones), the
+# shared headers and, for the tiled kernels, the tile plan
+_CSRC = "sparse_moe_expert_route_amd/csrc/"
+GEMM_SOURCES = {
+    ("mxfp4", "stream"): [_CSRC + "expert_gemm.hip", _CSRC + "moe_internal.h", _CSRC + "moe_launch.h"],
+    ("mxfp4", "tiled"): [_CSRC + "expert_gemm_tiled.hip", _CSRC + "moe_internal.h", _CSRC + "moe_launch.h",
+                         _CSRC + "permute.hip"],
+    ("fp8_block", "stream"): [_CSRC + "expert_gemm_fp8.hip", _CSRC + "moe_internal.h", _CSRC + "moe_launch.h"],
+    ("fp8_block", "tiled"): [_CSRC + "expert_gemm_fp8_tiled.hip", _CSRC + "moe_internal.h", _CSRC + "moe_launch.h",
+                             _CSRC + "permute.hip"],
+}
 
 
 def measured_traffic(workload, sources):
@@ -291,9 +292,9 @@ def main():
         achieved = gemm1_flops / (gemm1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4), "traffic": None}
-    roof["traffic"] = None if args.canonical_weights else \
-        measured_traffic(args.config, FP8_GEMM_SOURCES if fp8 else GEMM_SOURCES)
     tiled = N >= 32 * E and H % 512 == 0 and inter % 512 == 0 and max(H, inter) <= (8192 if fp8 else 6144)
+    roof["traffic"] = None if args.canonical_weights else \
+        measured_traffic(args.config, GEMM_SOURCES[("fp8_block" if fp8 else "mxfp4", "tiled" if tiled else "stream")])
     roof["kernel"] = "expert_gemm_%s%s_kernel<gate/up + SwiGLU + FP8 requant>" % ("fp8_" if fp8 else "",
                                                                                    "tiled" if tiled else "stream")
     roof["launch_ms"] = round(gemm1_ms, 4)
@@ -487,7 +488,8 @@ def micro():
     buf.fill_(1)
     sink = torch.empty(16384 * 256, dtype=torch.int32, device="cuda")
     hbm = {}
-    for pattern, name in ((0, "read_grid_stride"), (1, "read_chunk_per_workgroup")):
+    for pattern, name in ((0, "read_grid_stride"), (1, "read_chunk_per_workgroup"),
+                          (2, "read_grid_stride_nontemporal"), (3, "read_chunk_per_workgroup_nontemporal")):
         res = {}
         for grid in (1024, 2048, 4096, 8192, 16384):
             def run(g=grid, pt=pattern):
@@ -495,6 +497,26 @@ def micro():
             res[grid] = round(nbytes / timed(run) / 1e9, 1)
         hbm[name] = {"GB/s by grid": res, "best GB/s": max(res.values())}
         log("micro: %s %s" % (name, res))
+    # the packed-weight read pattern of the streaming GEMMs: 16 groups of one
+    # 16-row weight group each per workgroup (group bytes 16 K/2: 16 KiB for
+    # K = 2048, 32 KiB for 4096, 48 KiB for 6144), groups back to back or
+    # spaced by one extra KiB, waves walking the stages in step or staggered
+    L.moe_micro_hbm_read_groups.argtypes = [vp, sz, sz, sz, i32, vp, i32, vp]
+    gb = 2 << 30
+    groups = {}
+    for gk in (16, 32, 48):
+        for pad in (0, 1):
+            for skew in (0, 1, 2):
+                for nt in (0, 1):
+                    def rung(g=gk << 10, st=(gk + pad) << 10, sk=skew, n=nt):
+                        assert L.moe_micro_hbm_read_groups(vp(buf.data_ptr()), gb, g, st, sk, vp(sink.data_ptr()),
+                                                           n, sp) == 0
+                    nreg = gb // (16 * ((gk + pad) << 10))
+                    key = "group %d KiB%s, skew %d, %s" % (gk, " +1 KiB" if pad else "", skew,
+                                                         "non-temporal" if nt else "cached")
+                    groups[key] = round(nreg * 16 * (gk << 10) / timed(rung) / 1e9, 1)
+                    log("micro: read_gemm_groups %s: %s GB/s" % (key, groups[key]))
+    hbm["read_gemm_groups"] = groups
     res = {}
     for grid in (2048, 8192):
         def runw(g=grid):

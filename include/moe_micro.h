@@ -27,9 +27,22 @@ typedef struct ihipStream_t* hipStream_t;
 /* Read `bytes` (a multiple of 16) of buf with 16-byte loads, four in flight
  * per lane, `grid` workgroups of 256 threads.  pattern 0: grid-stride (each
  * load instruction of a wave covers 1 KiB of consecutive bytes); pattern 1:
- * one contiguous chunk per workgroup.  out [grid * 256] uint32 receives the
- * XOR of what each thread read.                                            */
+ * one contiguous chunk per workgroup; patterns 2 and 3: the same two with
+ * non-temporal loads.  out [grid * 256] uint32 receives the XOR of what each
+ * thread read.                                                             */
 int moe_micro_hbm_read(const void* buf, size_t bytes, uint32_t* out, int grid, int pattern, hipStream_t stream);
+
+/* Read floor(bytes / (16 group_stride)) regions in the pattern of the
+ * streaming expert GEMMs over packed weights: one workgroup of 4 waves per
+ * region of 16 groups of group_bytes (a multiple of 4 KiB holding an even
+ * number of 2 KiB stages), group_stride bytes apart; wave w reads groups
+ * 4w .. 4w+3 in 1 KiB blocks, two blocks per group per stage, two stages in
+ * flight.  skew 0: every wave walks the stages from the first; 1: wave w
+ * starts at stage w * nstage / 4; 2: workgroup b starts at (b mod 8) *
+ * nstage / 8 (both wrap around).  nontemporal != 0: non-temporal loads.
+ * out [grid * 256] uint32 receives the XOR of what each thread read.       */
+int moe_micro_hbm_read_groups(const void* buf, size_t bytes, size_t group_bytes, size_t group_stride, int skew,
+                              uint32_t* out, int nontemporal, hipStream_t stream);
 
 /* Write `bytes` (a multiple of 16) of buf with 16-byte grid-stride stores.  */
 int moe_micro_hbm_write(void* buf, size_t bytes, int grid, hipStream_t stream);

@@ -71,8 +71,20 @@ __host__ __device__ constexpr int stream_lds_bytes(int K) { return 256 * (K / 32
 __host__ __device__ constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // global loads of one pipeline stage (S steps of 128 K) at K offset kk:
-// 4*S weight loads and 2*S activation loads of 16 bytes per lane
-template <int S, bool PK>
+// 4*S weight loads and 2*S activation loads of 16 bytes per lane.  NT:
+// non-temporal weight loads (the weights are read once per m-tile).
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ uint4 load_weight16(const uint8_t* p) {
+    if constexpr (NT) {
+        const v4u32 v = __builtin_nontemporal_load((const v4u32*)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *(const uint4*)p;
+    }
+}
+
+template <int S, bool PK, bool NT>
 __device__ __forceinline__ void load_stage_mem(const Ptrs& P, int kk, Stage<S>& st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -80,8 +92,8 @@ __device__ __forceinline__ void load_stage_mem(const Ptrs& P, int kk, Stage<S>& 
         for (int s = 0; s < S; ++s) {
             // canonical: 64 bytes of the row per step; packed: one 1 KB block
             // (16 rows x 64 bytes) per step, lane l at 16 l
-            if constexpr (PK) st.w[j][s] = *(const uint4*)(P.w[j] + 8 * kk + 1024 * s);
-            else st.w[j][s] = *(const uint4*)(P.w[j] + kk / 2 + 64 * s);
+            if constexpr (PK) st.w[j][s] = load_weight16<NT>(P.w[j] + 8 * kk + 1024 * s);
+            else st.w[j][s] = load_weight16<NT>(P.w[j] + kk / 2 + 64 * s);
         }
     }
 #pragma unroll
@@ -130,10 +142,10 @@ __device__ __forceinline__ void load_stage_gscales(const Ptrs& P, int kk, Stage<
     for (int s = 0; s < S; ++s) st.xs[s] = __atomic_load_n(P.xs + kk / kFp8Block + s, __ATOMIC_RELAXED);
 }
 
-template <int S, bool SL, bool PK>
+template <int S, bool SL, bool PK, bool NT>
 __device__ __forceinline__ Stage<S> load_stage(const Ptrs& P, int kk) {
     Stage<S> st;
-    load_stage_mem<S, PK>(P, kk, st);
+    load_stage_mem<S, PK, NT>(P, kk, st);
     if constexpr (SL) load_stage_lds<S, PK>(P, kk, st);
     else load_stage_gscales<S, PK>(P, kk, st);
     return st;
@@ -203,7 +215,7 @@ __device__ __forceinline__ void stage_scales_issue(const GemmArgs& a, int e, int
     }
 }
 
-template <int MODE, int S, bool SL, bool PK>
+template <int MODE, int S, bool SL, bool PK, bool NT>
 __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r = lane & 15;
@@ -271,8 +283,23 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     // end re-read the last stage (an L2 hit) so that every load is unconditional.
     // The scheduling barriers keep each phase's instructions in place, so the
     // in-order load counter lets every wait cover exactly one stage.
+    //
+    // Wave w walks the K stages starting at stage w * nstage / 4, wrapping
+    // around.  The 16 weight-row groups of a workgroup lie K/2 * 16 bytes apart
+    // (16 or 32 KiB for K = 2048 or 4096); read in step, the four waves' loads
+    // fall on the same few HBM channels, and staggered they spread (in the
+    // packed-weight read pattern of the microbenchmark: 5.35 -> 6.05 TB/s at
+    // 32 KiB, 5.56 -> 6.10 at 16 KiB).  Each wave sums its own rows, so only the
+    // order of its fp32 additions changes.
     constexpr int KS = 128 * S;
-    const int klast = K - KS;
+    const int nstage = K / KS;
+    const int st0 = __builtin_amdgcn_readfirstlane(wave * nstage / 4);
+    // K offset of the wave's i-th stage (past the last: the last again)
+    auto koff = [&](int i) __attribute__((always_inline)) {
+        int q = min(i, nstage - 1) + st0;
+        q = q >= nstage ? q - nstage : q;
+        return q * KS;
+    };
     Stage<S> s0, s1;
     if constexpr (SL) {
         // the scale copy overlaps the first two stages' weight and activation
@@ -280,31 +307,31 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
         // the two stages issue kStageLoads loads each), then barrier
         stage_scales_issue<MODE, PK>(a, e, K, row0, nrows);
         __builtin_amdgcn_sched_barrier(0);
-        load_stage_mem<S, PK>(P, 0, s0);
-        load_stage_mem<S, PK>(P, min(KS, klast), s1);
+        load_stage_mem<S, PK, NT>(P, koff(0), s0);
+        load_stage_mem<S, PK, NT>(P, koff(1), s1);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kStageLoads));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         if (!live) return;
-        load_stage_lds<S, PK>(P, 0, s0);
-        load_stage_lds<S, PK>(P, min(KS, klast), s1);
+        load_stage_lds<S, PK>(P, koff(0), s0);
+        load_stage_lds<S, PK>(P, koff(1), s1);
     } else {
-        s0 = load_stage<S, SL, PK>(P, 0);
-        s1 = load_stage<S, SL, PK>(P, min(KS, klast));
+        s0 = load_stage<S, SL, PK, NT>(P, koff(0));
+        s1 = load_stage<S, SL, PK, NT>(P, koff(1));
     }
-    int kk = 0;
-    for (; kk + 2 * KS <= K; kk += 2 * KS) {
+    int i = 0;
+    for (; i + 2 <= nstage; i += 2) {
         compute_stage<S, SL>(s0, acc, gshift);
         __builtin_amdgcn_sched_barrier(0);
-        s0 = load_stage<S, SL, PK>(P, min(kk + 2 * KS, klast));
+        s0 = load_stage<S, SL, PK, NT>(P, koff(i + 2));
         __builtin_amdgcn_sched_barrier(0);
         compute_stage<S, SL>(s1, acc, gshift);
         __builtin_amdgcn_sched_barrier(0);
-        s1 = load_stage<S, SL, PK>(P, min(kk + 3 * KS, klast));
+        s1 = load_stage<S, SL, PK, NT>(P, koff(i + 3));
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (kk < K) compute_stage<S, SL>(s0, acc, gshift);   // odd number of stages: the last one is in s0
+    if (i < nstage) compute_stage<S, SL>(s0, acc, gshift);   // odd number of stages: the last one is in s0
 
     // ---- epilogues ----
     const int orow = row0 + r;
@@ -352,7 +379,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_stream_kernel(GemmArgs a) 
     }
 }
 
-template <int MODE, bool PK>
+template <int MODE, bool PK, bool NT>
 static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     // grid.y: upper bound on m-tiles (sum over experts of ceil(n_e / 16));
     // workgroups past the real tile count exit at once.
@@ -364,17 +391,23 @@ static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
     // Scales are staged in LDS once per workgroup where they fit: per-stage
     // scale loads would cost as many memory requests as the weights.
     if (K % 512 == 0 && stream_lds_bytes(K) <= 65536)
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, true, PK>), grid, block, stream_lds_bytes(K), stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, true, PK, NT>), grid, block, stream_lds_bytes(K), stream, a);
     else if (K % 256 == 0)
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, false, PK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 2, false, PK, NT>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1, false, PK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_stream_kernel<MODE, 1, false, PK, NT>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 template <int MODE>
 static hipError_t launch_mode(const GemmArgs& a, int K, hipStream_t stream) {
-    return a.packed ? launch_mode<MODE, true>(a, K, stream) : launch_mode<MODE, false>(a, K, stream);
+    // Non-temporal weight loads where each weight-row group is long (K >= 6144:
+    // 48 KiB per 16-row group and more).  In the microbenchmark of the packed
+    // read pattern (staggered waves) they read 6.39 against 6.03 TB/s at 48 KiB
+    // groups, the same at 32 KiB and less at 16 KiB (5.82 against 6.10).
+    const bool nt = K >= 6144;
+    if (a.packed) return nt ? launch_mode<MODE, true, true>(a, K, stream) : launch_mode<MODE, true, false>(a, K, stream);
+    return nt ? launch_mode<MODE, false, true>(a, K, stream) : launch_mode<MODE, false, false>(a, K, stream);
 }
 
 hipError_t launch_expert_gemm(GemmMode mode, const GemmArgs& a, hipStream_t stream) {

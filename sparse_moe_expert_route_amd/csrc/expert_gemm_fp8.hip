@@ -51,7 +51,19 @@ __device__ __forceinline__ v4f mfma_f8f8(v8i a, v8i b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, 127);
 }
 
-template <int S, bool PK>
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+// NT: a non-temporal load (the weights are read once per m-tile)
+template <bool NT>
+__device__ __forceinline__ uint4 load_weight16(const uint8_t* p) {
+    if constexpr (NT) {
+        const v4u32 v = __builtin_nontemporal_load((const v4u32*)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *(const uint4*)p;
+    }
+}
+
+template <int S, bool PK, bool NT>
 __device__ __forceinline__ StageF8<S> load_stage(const PtrsF8& P, int kk, int K) {
     StageF8<S> st;
     const int kb = kk / kFp8Block;
@@ -63,11 +75,11 @@ __device__ __forceinline__ StageF8<S> load_stage(const PtrsF8& P, int kk, int K)
             // 0..15 at 16 l and 16..31 at 1024 + 16 l; canonical: the row's
             // bytes 16g and 64 + 16g of the K block
             if constexpr (PK) {
-                st.w[j][s][0] = *(const uint4*)(P.w[j] + 2048 * (kb + s));
-                st.w[j][s][1] = *(const uint4*)(P.w[j] + 2048 * (kb + s) + 1024);
+                st.w[j][s][0] = load_weight16<NT>(P.w[j] + 2048 * (kb + s));
+                st.w[j][s][1] = load_weight16<NT>(P.w[j] + 2048 * (kb + s) + 1024);
             } else {
-                st.w[j][s][0] = *(const uint4*)(P.w[j] + kk + 128 * s);
-                st.w[j][s][1] = *(const uint4*)(P.w[j] + kk + 128 * s + 64);
+                st.w[j][s][0] = load_weight16<NT>(P.w[j] + kk + 128 * s);
+                st.w[j][s][1] = load_weight16<NT>(P.w[j] + kk + 128 * s + 64);
             }
         }
     }
@@ -110,7 +122,7 @@ __device__ __forceinline__ void compute_stage(const StageF8<S>& st, v4f (&acc)[4
 
 }  // namespace
 
-template <int MODE, int S, bool PK>
+template <int MODE, int S, bool PK, bool NT>
 __global__ void __launch_bounds__(256, 2) expert_gemm_fp8_stream_kernel(GemmArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -165,22 +177,32 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_fp8_stream_kernel(GemmArgs
     // two register stages in a copy-free ping-pong: while one stage is
     // multiplied the other one's loads are in flight.  Loads past the end
     // re-read the last stage (an L2 hit) so that every load is unconditional.
+    // Wave w walks the stages starting at stage w * nstage / 4, wrapping
+    // around, so that the four waves' loads of the workgroup's weight-row
+    // groups (16 K bytes apart) do not fall on the same HBM channels at once;
+    // only the order of each wave's fp32 additions changes.
     constexpr int KS = 128 * S;
-    const int klast = K - KS;
-    StageF8<S> s0 = load_stage<S, PK>(P, 0, K);
-    StageF8<S> s1 = load_stage<S, PK>(P, min(KS, klast), K);
-    int kk = 0;
-    for (; kk + 2 * KS <= K; kk += 2 * KS) {
+    const int nstage = K / KS;
+    const int st0 = __builtin_amdgcn_readfirstlane(wave * nstage / 4);
+    auto koff = [&](int i) __attribute__((always_inline)) {
+        int q = min(i, nstage - 1) + st0;
+        q = q >= nstage ? q - nstage : q;
+        return q * KS;
+    };
+    StageF8<S> s0 = load_stage<S, PK, NT>(P, koff(0), K);
+    StageF8<S> s1 = load_stage<S, PK, NT>(P, koff(1), K);
+    int i = 0;
+    for (; i + 2 <= nstage; i += 2) {
         compute_stage<MODE, S>(s0, acc);
         __builtin_amdgcn_sched_barrier(0);
-        s0 = load_stage<S, PK>(P, min(kk + 2 * KS, klast), K);
+        s0 = load_stage<S, PK, NT>(P, koff(i + 2), K);
         __builtin_amdgcn_sched_barrier(0);
         compute_stage<MODE, S>(s1, acc);
         __builtin_amdgcn_sched_barrier(0);
-        s1 = load_stage<S, PK>(P, min(kk + 3 * KS, klast), K);
+        s1 = load_stage<S, PK, NT>(P, koff(i + 3), K);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (kk < K) compute_stage<MODE, S>(s0, acc);   // odd number of stages: the last one is in s0
+    if (i < nstage) compute_stage<MODE, S>(s0, acc);   // odd number of stages: the last one is in s0
 
     // ---- epilogues ----
     const int orow = row0 + r;
@@ -230,7 +252,7 @@ __global__ void __launch_bounds__(256, 2) expert_gemm_fp8_stream_kernel(GemmArgs
     }
 }
 
-template <int MODE, bool PK>
+template <int MODE, bool PK, bool NT>
 static hipError_t launch_fp8_mode(const GemmArgs& a, int K, hipStream_t stream) {
     // grid.y: upper bound on m-tiles (sum over experts of ceil(n_e / 16));
     // workgroups past the real tile count exit at once.
@@ -238,15 +260,17 @@ static hipError_t launch_fp8_mode(const GemmArgs& a, int K, hipStream_t stream) 
     const int gx = (MODE == kGemm2) ? (a.H + 255) / 256 : a.I / 128;
     dim3 grid(gx, (unsigned)tiles), block(256);
     if (K % 256 == 0)
-        hipLaunchKernelGGL((expert_gemm_fp8_stream_kernel<MODE, 2, PK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_fp8_stream_kernel<MODE, 2, PK, NT>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((expert_gemm_fp8_stream_kernel<MODE, 1, PK>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((expert_gemm_fp8_stream_kernel<MODE, 1, PK, NT>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 template <int MODE>
 static hipError_t launch_fp8_mode(const GemmArgs& a, int K, hipStream_t stream) {
-    return a.packed ? launch_fp8_mode<MODE, true>(a, K, stream) : launch_fp8_mode<MODE, false>(a, K, stream);
+    const bool nt = K >= 6144;   // non-temporal weight loads for long weight-row groups
+    if (a.packed) return nt ? launch_fp8_mode<MODE, true, true>(a, K, stream) : launch_fp8_mode<MODE, true, false>(a, K, stream);
+    return nt ? launch_fp8_mode<MODE, false, true>(a, K, stream) : launch_fp8_mode<MODE, false, false>(a, K, stream);
 }
 
 hipError_t launch_expert_gemm_fp8(GemmMode mode, const GemmArgs& a, hipStream_t stream) {

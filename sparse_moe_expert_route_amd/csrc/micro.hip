@@ -21,26 +21,35 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 // ---- HBM ------------------------------------------------------------------
 
-// Four 16-byte loads in flight per lane per iteration (ordinary cached loads,
-// as the GEMMs' weight loads); the XOR of everything
-// read is stored per thread so that no load is dead.
+// Four 16-byte loads in flight per lane per iteration; NT = false: ordinary
+// cached loads (as the GEMMs' weight loads), true: non-temporal loads (as the
+// combine's).  The XOR of everything read is stored per thread so that no
+// load is dead.
+template <bool NT>
+__device__ __forceinline__ v4u ld16(const v4u* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
 __global__ void __launch_bounds__(256) read_grid_stride_kernel(const v4u* __restrict__ buf, size_t n16,
                                                                uint32_t* __restrict__ out) {
     const size_t stride = (size_t)gridDim.x * 256;
     size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     uint32_t x = 0;
     for (; i + 3 * stride < n16; i += 4 * stride) {
-        const v4u a = buf[i], b = buf[i + stride];
-        const v4u c = buf[i + 2 * stride], d = buf[i + 3 * stride];
+        const v4u a = ld16<NT>(buf + i), b = ld16<NT>(buf + i + stride);
+        const v4u c = ld16<NT>(buf + i + 2 * stride), d = ld16<NT>(buf + i + 3 * stride);
         x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
     }
     for (; i < n16; i += stride) {
-        const v4u a = buf[i];
+        const v4u a = ld16<NT>(buf + i);
         x ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
+template <bool NT>
 __global__ void __launch_bounds__(256) read_chunk_kernel(const v4u* __restrict__ buf, size_t n16,
                                                          uint32_t* __restrict__ out) {
     const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
@@ -48,14 +57,55 @@ __global__ void __launch_bounds__(256) read_chunk_kernel(const v4u* __restrict__
     uint32_t x = 0;
     size_t i = lo + threadIdx.x;
     for (; i + 3 * 256 < hi; i += 4 * 256) {
-        const v4u a = buf[i], b = buf[i + 256];
-        const v4u c = buf[i + 512], d = buf[i + 768];
+        const v4u a = ld16<NT>(buf + i), b = ld16<NT>(buf + i + 256);
+        const v4u c = ld16<NT>(buf + i + 512), d = ld16<NT>(buf + i + 768);
         x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
     }
     for (; i < hi; i += 256) {
-        const v4u a = buf[i];
+        const v4u a = ld16<NT>(buf + i);
         x ^= a.x ^ a.y ^ a.z ^ a.w;
     }
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
+// The read pattern of the streaming expert GEMMs over packed weights: each
+// workgroup owns a region of 16 groups (one 16-row group of weight rows
+// each) of gbytes, gstride bytes apart (gstride >= gbytes; the region is
+// 16 gstride); wave w reads groups 4w .. 4w+3, each in 1 KB blocks (lane l at
+// 16 l), two blocks per group per stage and two stages in flight: 16 loads of
+// 16 bytes per lane outstanding, as in the GEMMs.  skew 1: wave w walks its
+// stages starting at w nstage / 4 (wrapping), skew 2: at (blockIdx mod 8)
+// nstage / 8, skew 0: all from stage 0.
+template <bool NT>
+__global__ void __launch_bounds__(256) read_groups_kernel(const uint8_t* __restrict__ buf, size_t gbytes,
+                                                          size_t gstride, int skew, uint32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint8_t* base = buf + (size_t)blockIdx.x * 16 * gstride + (size_t)(4 * wave) * gstride + 16 * lane;
+    const int nstage = (int)(gbytes / 2048);
+    const int st0 = skew == 1 ? wave * nstage / 4 : skew == 2 ? (int)(blockIdx.x & 7) * nstage / 8 : 0;
+    uint32_t x = 0;
+    v4u a[2][8];
+    auto issue = [&](int b, int st) __attribute__((always_inline)) {
+        int sp = st + st0;
+        sp = sp >= nstage ? sp - nstage : sp;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            a[b][q] = ld16<NT>((const v4u*)(base + (size_t)(q >> 1) * gstride + (size_t)sp * 2048 + 1024 * (q & 1)));
+    };
+    auto use = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x ^= a[b][q].x ^ a[b][q].y ^ a[b][q].z ^ a[b][q].w;
+    };
+    issue(0, 0);
+    issue(1, nstage > 1 ? 1 : 0);
+    for (int st = 0; st < nstage; st += 2) {
+        use(0);
+        issue(0, st + 2 < nstage ? st + 2 : nstage - 1);
+        use(1);
+        issue(1, st + 3 < nstage ? st + 3 : nstage - 1);
+    }
+    use(0);
+    use(1);
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
@@ -146,17 +196,40 @@ hipError_t launch_mfma(int shape, int iters, int grid, float* out, unsigned long
     return hipGetLastError();
 }
 
+// an even number of 2 KB stages per group (the read loop takes two at a time)
+inline int nstage_even(size_t group_bytes) { return (group_bytes / 2048) % 2 == 0; }
+
 }  // namespace
 
 extern "C" {
 
 int moe_micro_hbm_read(const void* buf, size_t bytes, uint32_t* out, int grid, int pattern, hipStream_t stream) {
-    if (!buf || !out || grid <= 0 || bytes < 16 || (bytes & 15) || (pattern != 0 && pattern != 1)) return 1;
-    if (pattern == 0)
-        hipLaunchKernelGGL(read_grid_stride_kernel, dim3(grid), dim3(256), 0, stream, (const v4u*)buf, bytes / 16,
-                           out);
+    if (!buf || !out || grid <= 0 || bytes < 16 || (bytes & 15) || pattern < 0 || pattern > 3) return 1;
+    const v4u* b = (const v4u*)buf;
+    switch (pattern) {
+        case 0: hipLaunchKernelGGL(read_grid_stride_kernel<false>, dim3(grid), dim3(256), 0, stream, b, bytes / 16, out); break;
+        case 1: hipLaunchKernelGGL(read_chunk_kernel<false>, dim3(grid), dim3(256), 0, stream, b, bytes / 16, out); break;
+        case 2: hipLaunchKernelGGL(read_grid_stride_kernel<true>, dim3(grid), dim3(256), 0, stream, b, bytes / 16, out); break;
+        default: hipLaunchKernelGGL(read_chunk_kernel<true>, dim3(grid), dim3(256), 0, stream, b, bytes / 16, out); break;
+    }
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int moe_micro_hbm_read_groups(const void* buf, size_t bytes, size_t group_bytes, size_t group_stride, int skew,
+                              uint32_t* out, int nontemporal, hipStream_t stream) {
+    if (!buf || !out || group_bytes < 4096 || (group_bytes & 4095) || (nstage_even(group_bytes) == 0) ||
+        group_stride < group_bytes || (group_stride & 15) || skew < 0 || skew > 2)
+        return 1;
+    const size_t region = 16 * group_stride;
+    if (bytes < region) return 1;
+    const size_t grid = bytes / region;
+    if (grid > (size_t)1 << 20) return 1;
+    if (nontemporal)
+        hipLaunchKernelGGL(read_groups_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint8_t*)buf,
+                           group_bytes, group_stride, skew, out);
     else
-        hipLaunchKernelGGL(read_chunk_kernel, dim3(grid), dim3(256), 0, stream, (const v4u*)buf, bytes / 16, out);
+        hipLaunchKernelGGL(read_groups_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, (const uint8_t*)buf,
+                           group_bytes, group_stride, skew, out);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -43,7 +43,7 @@ def test_micro_library_exports_every_declared_symbol():
         B.build()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_micro.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(moe_micro_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["moe_micro_hbm_read", "moe_micro_hbm_write", "moe_micro_mfma"]
+    assert names == ["moe_micro_hbm_read", "moe_micro_hbm_read_groups", "moe_micro_hbm_write", "moe_micro_mfma"]
     L = ctypes.CDLL(B.MICRO_LIB)
     for n in names:
         assert hasattr(L, n), n
