@@ -231,13 +231,28 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
         // two MFMAs into a fresh partial, then acc += partial * (weight scale x
         // token scale).  Two partials alternate between the token tiles: the
         // MFMAs of tile j run on the matrix core while the vector ALU scales
-        // and adds the partial of tile j - 1 (half of it after each MFMA).
-        // The scheduling barriers fix that order and keep the compiler from
-        // hoisting every LDS read (which costs registers the weights need).
+        // and adds the partial of tile j - 1 (half of it after each MFMA).  The
+        // LDS operands of the next (block, tile) pair are read while the
+        // current pair is multiplied, so their latency is not waited out before
+        // each MFMA.  The scheduling barriers fix that order and keep the
+        // compiler from hoisting every LDS read (which costs registers the
+        // weights need).
         auto compute = [&](int st, int buf) __attribute__((always_inline)) {
             const uint8_t* lds = f8_lds.act[buf];
             const float* xsl = f8_lds.xsc[buf];
             const int wnext = min(st + 1, nstage - 1);
+            // steps 2b and 2b+1 of row 32j + r: chunks 4s + g and 4s + 2 + g
+            // (the row's swizzle depends on r only: 32j adds a constant), and
+            // the row's activation scale of block b
+            v8i Bn0, Bn1;
+            float sxn;
+            auto read_ops = [&](int b, int j) __attribute__((always_inline)) {
+                const uint8_t* rowp = lds + (32 * j) * kF8StageK + lane_row;
+                Bn0 = cat8(*(const v4i*)(rowp + slot[b][0]), *(const v4i*)(rowp + slot[b][1]));
+                Bn1 = cat8(*(const v4i*)(rowp + slot[b][2]), *(const v4i*)(rowp + slot[b][3]));
+                sxn = xsl[2 * (32 * j + r) + b];
+            };
+            read_ops(0, 0);
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 // (from LDS: a global load here would make the in-order load
@@ -255,14 +270,12 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
                 };
 #pragma unroll
                 for (int j = 0; j < kF8TT; ++j) {
-                    // steps 2b and 2b+1: chunks 4s + g and 4s + 2 + g of row 32j + r
-                    // (the row's swizzle depends on r only: 32j adds a constant)
-                    const uint8_t* rowp = lds + (32 * j) * kF8StageK + lane_row;
-                    const v8i B0 = cat8(*(const v4i*)(rowp + slot[b][0]), *(const v4i*)(rowp + slot[b][1]));
-                    const v8i B1 = cat8(*(const v4i*)(rowp + slot[b][2]), *(const v4i*)(rowp + slot[b][3]));
-                    const float sx = xsl[2 * (32 * j + r) + b];
+                    const v8i B0 = Bn0, B1 = Bn1;
+                    const float sx = sxn;
                     part[j & 1] = mfma32_f8f8(A0, B0, v16f{});
                     __builtin_amdgcn_sched_barrier(0);
+                    if (j + 1 < kF8TT) read_ops(b, j + 1);
+                    else if (b == 0) read_ops(1, 0);
                     if (j > 0) rescale(j - 1, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     part[j & 1] = mfma32_f8f8(A1, B1, part[j & 1]);
