@@ -270,6 +270,16 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
                 };
 #pragma unroll
                 for (int j = 0; j < kF8TT; ++j) {
+                    // The older wave of a SIMD would otherwise take every MFMA
+                    // issue slot until it stalls; a priority that falls through
+                    // the stage lets the wave that is behind issue first, which
+                    // keeps the two waves of a SIMD apart
+                    switch ((kF8TT * b + j) >> 1) {
+                        case 0: __builtin_amdgcn_s_setprio(3); break;
+                        case 1: __builtin_amdgcn_s_setprio(2); break;
+                        case 2: __builtin_amdgcn_s_setprio(1); break;
+                        default: __builtin_amdgcn_s_setprio(0); break;
+                    }
                     const v8i B0 = Bn0, B1 = Bn1;
                     const float sx = sxn;
                     part[j & 1] = mfma32_f8f8(A0, B0, v16f{});
