@@ -8,7 +8,7 @@ namespace moe {
 
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_perm,
+__global__ void __launch_bounds__(512) combine_kernel(const float* __restrict__ y_perm,
                                                       const int32_t* __restrict__ row_of_slot,
                                                       const float* __restrict__ w, void* __restrict__ y,
                                                       int out_bf16, int T, int H, int k) {
@@ -26,13 +26,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     bool has[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) has[j] = (unsigned)rows[j] < (unsigned)(T * k);
-    // workgroup (t, b) covers channels [1024 b, 1024 b + 1024): a decode step
+    // workgroup (t, b) covers channels [2048 b, 2048 b + 2048): a decode step
     // with few tokens still spreads over the whole chip.  All eight loads are
     // issued before the first FMA (slots past k re-read slot k-1 with weight
     // 0, which leaves the sum unchanged but for the sign of an all-zero sum),
     // and they bypass the caches: y_perm is read once.  The stores of y bypass
     // them too (on Pro skewed prefill, 384 MiB of y: combine 732 -> 687 us).
-    for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < H; c += gridDim.y * 256 * 4) {
+    for (int c = (blockIdx.y * 512 + threadIdx.x) * 4; c < H; c += gridDim.y * 512 * 4) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
         v4f v[8];
 #pragma unroll
@@ -59,11 +59,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const float* y_perm, const int32_t* row_of_slot, const float* w, void* y, int out_bf16,
                           int64_t T, int H, int k, hipStream_t stream) {
-    // few tokens (decode): spread each token over channel blocks of 1024 so
+    // few tokens (decode): spread each token over channel blocks of 2048 so
     // the combine still covers the chip; many tokens: one workgroup per token
-    // (fewer, longer workgroups: Flash prefill 238 -> 222 us)
-    const unsigned cb = T >= 2048 ? 1u : (unsigned)((H + 1023) / 1024);
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T, cb), dim3(256), 0, stream, y_perm, row_of_slot, w, y, out_bf16,
+    // (fewer, longer workgroups: Flash prefill 238 -> 222 us), of 512 threads
+    // (Pro skewed prefill 679 -> 667 us against 256 threads)
+    const unsigned cb = T >= 2048 ? 1u : (unsigned)((H + 2047) / 2048);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)T, cb), dim3(512), 0, stream, y_perm, row_of_slot, w, y, out_bf16,
                        (int)T, H, k);
     return hipGetLastError();
 }
