@@ -196,9 +196,6 @@ hipError_t launch_mfma(int shape, int iters, int grid, float* out, unsigned long
     return hipGetLastError();
 }
 
-// an even number of 2 KB stages per group (the read loop takes two at a time)
-inline int nstage_even(size_t group_bytes) { return (group_bytes / 2048) % 2 == 0; }
-
 }  // namespace
 
 extern "C" {
@@ -217,8 +214,9 @@ int moe_micro_hbm_read(const void* buf, size_t bytes, uint32_t* out, int grid, i
 
 int moe_micro_hbm_read_groups(const void* buf, size_t bytes, size_t group_bytes, size_t group_stride, int skew,
                               uint32_t* out, int nontemporal, hipStream_t stream) {
-    if (!buf || !out || group_bytes < 4096 || (group_bytes & 4095) || (nstage_even(group_bytes) == 0) ||
-        group_stride < group_bytes || (group_stride & 15) || skew < 0 || skew > 2)
+    // a multiple of 4 KiB: an even number of 2 KiB stages (the read loop takes two at a time)
+    if (!buf || !out || group_bytes < 4096 || (group_bytes & 4095) || group_stride < group_bytes ||
+        (group_stride & 15) || skew < 0 || skew > 2)
         return 1;
     const size_t region = 16 * group_stride;
     if (bytes < region) return 1;
