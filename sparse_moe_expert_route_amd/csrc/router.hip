@@ -235,13 +235,23 @@ __device__ __forceinline__ void router_tiled_kloop(const uint16_t* __restrict__ 
     __builtin_amdgcn_s_waitcnt(rt_vmcnt(0));
 }
 
+// Workgroup id -> tile: workgroups on XCD x (id mod 8) take the token blocks
+// x, x + 8, x + 16, ... (tpx of them) for expert block 0, then the same token
+// blocks for expert block 1, and so on.  The workgroups an XCD runs at one time
+// then share one or two expert blocks of W_r in its L2 (with every expert block
+// in flight at once, 384 x 6144 bf16 = 4.5 MiB does not fit one XCD's 4 MB)
+// and read the same token blocks of x.  Ids past the tiles exit at once.
 __global__ void __launch_bounds__(256) router_logits_tiled_kernel(const uint16_t* __restrict__ x,
                                                                    const uint16_t* __restrict__ wr,
-                                                                   float* __restrict__ logits, int T, int H, int E) {
+                                                                   float* __restrict__ logits, int T, int H, int E,
+                                                                   int tpx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, r = lane & 31;
     const int wm = wave & 1, wn = wave >> 1;
-    const int e0 = blockIdx.x * kRtExp, t0 = blockIdx.y * kRtTok;
+    const int local = (int)(blockIdx.x >> 3);
+    const int eb = local / tpx, tb = (local - eb * tpx) * 8 + (int)(blockIdx.x & 7);
+    const int e0 = eb * kRtExp, t0 = tb * kRtTok;
+    if (e0 >= E || t0 >= T) return;
     v16f_r acc[2];
     router_tiled_kloop(x, wr, T, H, E, t0, e0, acc, rt_buf0, rt_buf1, rt_buf2);
     // acc[j]: token t0 + 32wm + r, experts e0 + 64wn + 32j + 8q + 4g + (0..3)
@@ -288,10 +298,12 @@ hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, flo
         hipLaunchKernelGGL((router_logits_kernel<1, 4>), grid, dim3(256), 0, stream, x, w_router, logits,
                            (int)T, H, E);
     } else {
-        // prefill shapes: LDS-tiled, 64 tokens x 128 experts per workgroup,
-        // expert blocks fastest so the workgroups sharing a block of x run together
-        dim3 grid((E + kRtExp - 1) / kRtExp, (unsigned)((T + kRtTok - 1) / kRtTok));
-        hipLaunchKernelGGL(router_logits_tiled_kernel, grid, dim3(256), 0, stream, x, w_router, logits, (int)T, H, E);
+        // prefill shapes: LDS-tiled, 64 tokens x 128 experts per workgroup, an
+        // XCD's workgroups grouped by expert block (router_logits_tiled_kernel)
+        const int nbe = (E + kRtExp - 1) / kRtExp;
+        const int tpx = (int)(((T + kRtTok - 1) / kRtTok + 7) / 8);   // token blocks per XCD
+        hipLaunchKernelGGL(router_logits_tiled_kernel, dim3((unsigned)(nbe * tpx * 8)), dim3(256), 0, stream, x,
+                           w_router, logits, (int)T, H, E, tpx);
     }
     return hipGetLastError();
 }
