@@ -17,9 +17,10 @@
 // Streaming structure (weight-bandwidth-bound shapes): a workgroup owns one
 // m-tile of 16 rows of one expert and a block of weight rows; every weight
 // byte is read exactly once per m-tile, directly into registers, never
-// through LDS.  K is walked in natural order, 128 per MFMA, S MFMAs per
-// pipeline stage: one load instruction then covers 64 contiguous bytes of each
-// of 16 weight rows (4 lanes per row).  Lane (g, r) needs the scale of 32-block
+// through LDS.  K is walked 128 per MFMA, S MFMAs per pipeline stage: one load
+// instruction then covers 64 contiguous bytes of each of 16 weight rows (4
+// lanes per row).  Each wave starts its stages a quarter of K after the wave
+// before it and wraps around (see the K loop).  Lane (g, r) needs the scale of 32-block
 // 4s + g at step s: it loads the row's 4S scale bytes of the stage and shifts
 // byte g of word s to the bottom (op_sel 0).  The activation scale of step s is
 // the row's scale byte of that 128-channel block.
