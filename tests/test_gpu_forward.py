@@ -247,8 +247,8 @@ def test_forward_full_size_sampled(moe, cfg, packed, score):
 # skewed workload has ~10k rows: 80 m-tiles of 128 rows in chunks of four,
 # the last one partial.
 # ---------------------------------------------------------------------------
-STAGED_FULL = ["flash_decode", "flash_prefill", "pro_decode", "pro_skewed_prefill", "flash_prefill_tp4",
-               "pro_skewed_prefill_tp4", "flash_prefill_fp8"]
+STAGED_FULL = ["flash_decode", "flash_verify", "flash_prefill", "pro_decode", "pro_skewed_prefill", "flash_prefill_tp4",
+               "pro_skewed_prefill_tp4", "pro_decode_tp4", "flash_prefill_fp8", "flash_decode_fp8"]
 
 
 def _xcd_boundary_experts(counts, NB, rows_per_tile=128, xcds=8):
