@@ -157,11 +157,12 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
         const F8Item it = f8_item_at(a, item, NB);
         const int row0 = it.row0, nrows = it.nrows;
         // activation rows of this thread's stage loads and scale copy
-        int arow[kF8ActLoads];
+        uint32_t aoff[kF8ActLoads];   // byte offset of the thread's chunk in its activation row (< 2 GiB)
 #pragma unroll
         for (int p = 0; p < kF8ActLoads; ++p) {
             const int rr = row0 + min(srow[p], nrows - 1);
-            arow[p] = GATHER ? a.act_rows[rr] : rr;
+            const int arow = GATHER ? a.act_rows[rr] : rr;
+            aoff[p] = (uint32_t)arow * (uint32_t)K + 16 * schunk[p];
         }
         int xrow = row0 + min(xs_row, nrows - 1);
         if (GATHER) xrow = a.act_rows[xrow];
@@ -209,8 +210,10 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
         float xreg;
         auto load_act = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-            for (int p = 0; p < kF8ActLoads; ++p)
-                areg[p] = *(const v4i*)(a.act + (size_t)arow[p] * K + st * kF8StageK + 16 * schunk[p]);
+            for (int p = 0; p < kF8ActLoads; ++p) {
+                const uint8_t* base = a.act + st * kF8StageK;   // wave-uniform
+                areg[p] = *(const v4i*)(base + aoff[p]);
+            }
             xreg = asc[(size_t)xrow * KB + 2 * st + xs_blk];
         };
         auto store_act = [&](int buf) __attribute__((always_inline)) {
@@ -319,12 +322,15 @@ __global__ void __launch_bounds__(64 * kF8Waves, 1) expert_gemm_fp8_tiled_kernel
         // the MFMAs below the barrier and keep every LDS operand live.  Past
         // the last stage the loads repeat the last stage and the store fills the
         // idle buffer, which nobody reads.
-        for (int st = 0; st < nstage; ++st) {
-            const int buf = st & 1;
-            compute(st, buf);
-            store_act(buf ^ 1);                // stage st + 1 into the other buffer
+        for (int st = 0; st < nstage; st += 2) {   // nstage is even (K % 512 == 0)
+            compute(st, 0);
+            store_act(1);                      // stage st + 1 into the other buffer
             __syncthreads();
             load_act(min(st + 2, nstage - 1));
+            compute(st + 1, 1);
+            store_act(0);
+            __syncthreads();
+            load_act(min(st + 3, nstage - 1));
         }
 
         // ---- epilogues: lane holds tokens 32j + r and tile rows 8(i/4) + 4g + (i%4) ----
